@@ -46,6 +46,11 @@ from .spear_oracle import (  # noqa: F401
     quantize,
     pack_canonical,
     unpack_canonical,
+    NIBBLE_K,
+    interleave_nibbles,
+    deinterleave_nibbles,
+    place_words,
+    unplace_words,
     tile_words,
     untile_words,
     pack_w4,

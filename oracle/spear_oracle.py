@@ -96,18 +96,44 @@ def unpack_canonical(words):
 
 
 # --------------------------------------------------------------------------
-# Tiled layout (layout id 2).  K is padded to K_pad (multiple of 128) and N to
-# N_pad (multiple of 16) with code 8 (q = 0).  Canonical word (k8, n) goes to
-#     nb = n // 16, c = n % 16, kc = k8 // 16, j = (k8 % 16) // 4, t = k8 % 4
-#     index = ((nb * (K_pad/128) + kc) * 64 + (t * 16 + c)) * 4 + j
-# so each 16-column panel is contiguous over K, and in every 1 KiB tile
-# (16 columns x 128 k) the 16 bytes at slot L = t*16 + c hold, for the four
-# 32-k blocks j, the k-octet t of column c: the B operand a 64-lane
-# 16x16x32 matrix instruction takes from lane L.
+# Tiled layout (layout id 2).  Two steps on the canonical words:
+# (1) nibble interleave inside each word: bit field i (bits 4i..4i+3) holds
+#     k-offset NIBBLE_K[i] = (0, 2, 4, 6, 1, 3, 5, 7)[i], so that the 16-bit
+#     halves of (word >> 4j) & 0x000F000F are the codes of k-offsets 2j and
+#     2j+1, in that order;
+# (2) placement: K is padded to K_pad (multiple of 128) and N to N_pad
+#     (multiple of 16) with code 8 (q = 0), and word (k8, n) goes to
+#         nb = n // 16, c = n % 16, kc = k8 // 16, j = (k8 % 16) // 4, t = k8 % 4
+#         index = ((nb * (K_pad/128) + kc) * 64 + (t * 16 + c)) * 4 + j
+#     so each 16-column panel is contiguous over K, and in every 1 KiB tile
+#     (16 columns x 128 k) the 16 bytes at slot L = t*16 + c hold, for the four
+#     32-k blocks j, the k-octet t of column c: the B operand a 64-lane
+#     16x16x32 matrix instruction takes from lane L.
 # --------------------------------------------------------------------------
 
-def tile_words(words_c, K, N):
-    """Canonical words [K/8, N] -> flat tiled uint32 array (padded)."""
+NIBBLE_K = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def interleave_nibbles(words):
+    """Canonical words (k-offset i in field i) -> interleaved (NIBBLE_K order)."""
+    words = np.asarray(words, dtype=np.uint32)
+    out = np.zeros_like(words)
+    for field, koff in enumerate(NIBBLE_K):
+        out |= ((words >> np.uint32(4 * koff)) & np.uint32(0xF)) << np.uint32(4 * field)
+    return out
+
+
+def deinterleave_nibbles(words):
+    """Inverse of interleave_nibbles."""
+    words = np.asarray(words, dtype=np.uint32)
+    out = np.zeros_like(words)
+    for field, koff in enumerate(NIBBLE_K):
+        out |= ((words >> np.uint32(4 * field)) & np.uint32(0xF)) << np.uint32(4 * koff)
+    return out
+
+
+def place_words(words_c, K, N):
+    """Words [K/8, N] -> flat array in the tiled placement (padded with code 8)."""
     kp, np_ = padded_dims(K, N)
     full = np.full((kp // 8, np_), 0x88888888, dtype=np.uint32)
     full[: K // 8, :N] = words_c
@@ -116,8 +142,8 @@ def tile_words(words_c, K, N):
     return np.ascontiguousarray(t5.transpose(3, 0, 2, 4, 1)).reshape(-1)  # [nb, kc, t, c, j]
 
 
-def untile_words(flat, K, N):
-    """Flat tiled uint32 array -> canonical words [K/8, N] (padding dropped)."""
+def unplace_words(flat, K, N):
+    """Inverse of place_words (padding dropped)."""
     kp, np_ = padded_dims(K, N)
     kc_n, nb_n = kp // K_CHUNK, np_ // N_BLOCK
     flat = np.asarray(flat, dtype=np.uint32)
@@ -126,6 +152,16 @@ def untile_words(flat, K, N):
     t5 = flat.reshape(nb_n, kc_n, 4, 16, 4)           # [nb, kc, t, c, j]
     full = t5.transpose(1, 4, 2, 0, 3).reshape(kp // 8, np_)
     return np.ascontiguousarray(full[: K // 8, :N])
+
+
+def tile_words(words_c, K, N):
+    """Canonical words [K/8, N] -> flat layout-2 array (interleave, then place)."""
+    return place_words(interleave_nibbles(words_c), K, N)
+
+
+def untile_words(flat, K, N):
+    """Flat layout-2 array -> canonical words [K/8, N]."""
+    return deinterleave_nibbles(unplace_words(flat, K, N))
 
 
 def pack_w4(W):

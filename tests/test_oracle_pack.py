@@ -49,6 +49,31 @@ def test_golden_canonical_words():
         assert int(oracle.pack_canonical(q)[0, 0]) == int(ex["word"], 16), ex
 
 
+def test_golden_interleaved_words():
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    for ex in g["interleave_examples"]:
+        c = np.array([int(ex["canonical"], 16)], dtype=np.uint32)
+        i = oracle.interleave_nibbles(c)
+        assert int(i[0]) == int(ex["interleaved"], 16), ex
+        assert int(oracle.deinterleave_nibbles(i)[0]) == int(c[0])
+
+
+def test_interleave_gives_fp16_pairs_in_k_order():
+    """(word >> 4j) & 0x000F000F must hold k-offset 2j in the low half and
+    2j+1 in the high half: OR-ing 0x6400 makes each half the fp16 1024 + u."""
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        u = rng.integers(0, 16, size=8)
+        canon = np.array([sum(int(u[k]) << (4 * k) for k in range(8))], dtype=np.uint32)
+        w = int(oracle.interleave_nibbles(canon)[0])
+        for j in range(4):
+            pair = ((w >> (4 * j)) & 0x000F000F) | 0x64006400
+            lo = np.array([pair & 0xFFFF], dtype=np.uint16).view(np.float16)[0]
+            hi = np.array([pair >> 16], dtype=np.uint16).view(np.float16)[0]
+            assert float(lo) - 1032 == u[2 * j] - 8 and float(hi) - 1032 == u[2 * j + 1] - 8
+
+
 def test_golden_tiled_indexes():
     with open(GOLDEN) as f:
         g = json.load(f)
@@ -56,7 +81,7 @@ def test_golden_tiled_indexes():
         K, N = ex["K"], ex["N"]
         words = np.zeros((K // 8, N), dtype=np.uint32)
         words[ex["k8"], ex["n"]] = 0xDEADBEEF
-        flat = oracle.tile_words(words, K, N)
+        flat = oracle.place_words(words, K, N)
         assert flat.size == ex["total_words"] == oracle.packed_words(K, N)
         hits = np.nonzero(flat == 0xDEADBEEF)[0]
         assert list(hits) == [ex["index"]], ex
@@ -68,11 +93,12 @@ def test_tiling_is_bijection_and_pads_with_zero_code(K, N):
     words = rng.integers(0, 2 ** 32, size=(K // 8, N), dtype=np.uint64).astype(np.uint32)
     flat = oracle.tile_words(words, K, N)
     assert np.array_equal(oracle.untile_words(flat, K, N), words)
+    assert np.array_equal(oracle.unplace_words(oracle.place_words(words, K, N), K, N), words)
     kp, npad = oracle.padded_dims(K, N)
     assert flat.size == kp * npad // 8
     # positions that hold real words: where a permutation of 1..n lands
     ident = np.arange(1, words.size + 1, dtype=np.uint32).reshape(words.shape)
-    landed = oracle.tile_words(ident, K, N)
+    landed = oracle.place_words(ident, K, N)
     real = landed != 0x88888888
     assert real.sum() == words.size
     assert np.array_equal(np.sort(landed[real]), np.arange(1, words.size + 1))
@@ -97,7 +123,8 @@ def test_tile_slot_holds_matrix_instruction_b_operand():
                     col = nb * 16 + lane % 16
                     for e in range(8):
                         k = kb * 32 + 8 * (lane // 16) + e
-                        assert ((word >> (4 * e)) & 0xF) - 8 == q[k, col]
+                        field = e // 2 if e % 2 == 0 else 4 + e // 2
+                        assert ((word >> (4 * field)) & 0xF) - 8 == q[k, col]
 
 
 # ---------------------------------------------------------------- scales
