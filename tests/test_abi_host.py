@@ -1,0 +1,156 @@
+"""C-ABI library on the host (no GPU): it loads, exports every function the
+header declares, and its host-only paths (status strings, sizes, planning,
+argument checks) behave as documented.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4_gemm_gated_amd import _binding
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "spear_w4ec.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_binding.LIB_PATH),
+                                reason="libspear_w4ec.so not built (run __graft_entry__.build())")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _binding.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spear_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("spear_w4ec_linear", "spear_pack_w4", "spear_dispatch_plan"):
+        assert required in names
+    assert set(names) == set(_binding.EXPORTS)
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version(lib):
+    assert lib.spear_abi_version() == 1
+    for code, name in _binding.STATUS_NAMES.items():
+        assert lib.spear_status_str(code).decode().startswith(name)
+    assert lib.spear_status_str(99).decode() == "SPEAR_ERR_UNKNOWN"
+
+
+def test_packed_bytes(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.spear_packed_bytes(4096, 4096, ctypes.byref(out)) == 0 and out.value == 4096 * 4096 // 2
+    assert lib.spear_packed_bytes(136, 20, ctypes.byref(out)) == 0 and out.value == 256 * 32 // 2
+    assert lib.spear_packed_bytes(12, 20, ctypes.byref(out)) == 2
+    assert lib.spear_packed_bytes(0, 20, ctypes.byref(out)) == 2
+    assert lib.spear_packed_bytes(8, 0, ctypes.byref(out)) == 2
+    assert lib.spear_packed_bytes(8, 8, None) == 1
+
+
+def plan(lib, M, K, N, r, variant=0, cus=256, bias=0.0, tau=0.0):
+    d = _binding.LinearDesc(M, K, N, r, bias, tau, variant, cus)
+    p = _binding.Plan()
+    st = lib.spear_dispatch_plan(ctypes.byref(d), ctypes.byref(p))
+    return st, p
+
+
+def test_dispatch_rules(lib):
+    st, p = plan(lib, 16, 4096, 4096, 32)
+    assert st == 0 and p.variant in (1, 2) and p.kernel == 0 and p.workspace_bytes > 0
+    st, p = plan(lib, 2048, 4096, 14336, 64)
+    assert st == 0 and p.variant == 2 and p.kernel == 1 and p.workspace_bytes > 0
+    st, p = plan(lib, 16, 4096, 4096, 0)
+    assert st == 0 and p.variant == 3 and p.workspace_bytes == 0
+    st, p = plan(lib, 64, 4096, 4096, 32, variant=3)
+    assert st == 0 and p.variant == 3 and p.workspace_bytes == 0
+    st, p = plan(lib, 0, 512, 512, 16)
+    assert st == 0
+    assert p.abi_version == 1 and p.layout_id == 2 and p.cus == 256
+
+
+def test_dispatch_is_deterministic(lib):
+    a = plan(lib, 512, 14336, 4096, 64)[1].as_dict()
+    b = plan(lib, 512, 14336, 4096, 64)[1].as_dict()
+    assert a == b
+
+
+@pytest.mark.parametrize("M,K,N,r,code", [
+    (-1, 512, 512, 16, 2), (16, 12, 512, 16, 2), (16, 0, 512, 16, 2), (16, 512, 0, 16, 2),
+    (16, 512, 512, -1, 2), (16, 512, 512, 257, 2),
+])
+def test_dispatch_rejects_bad_shapes(lib, M, K, N, r, code):
+    assert plan(lib, M, K, N, r)[0] == code
+
+
+def test_dispatch_rejects_bad_arguments(lib):
+    assert plan(lib, 16, 512, 512, 16, variant=7)[0] == 8
+    assert plan(lib, 16, 512, 512, 16, bias=float("nan"))[0] == 8
+    assert plan(lib, 16, 512, 512, 16, tau=1.5)[0] == 8
+    assert plan(lib, 16, 512, 512, 16, tau=float("inf"))[0] == 8
+    assert lib.spear_dispatch_plan(None, None) == 1
+
+
+def test_linear_checks_before_launch(lib):
+    """Every one of these returns an error before anything is enqueued."""
+    st, p = plan(lib, 16, 512, 512, 16)
+    d = _binding.LinearDesc(16, 512, 512, 16, 0.0, 0.0, 0, 256)
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: checks fail first
+    odd = ctypes.c_void_p(0x1002)
+    null = ctypes.c_void_p(0)
+    ws = p.workspace_bytes
+    call = lambda *a: lib.spear_w4ec_linear(ctypes.byref(d), ctypes.byref(p), *a)  # noqa: E731
+    assert call(null, fake, fake, fake, fake, fake, fake, fake, ws, null) == 1
+    assert call(fake, fake, fake, null, fake, fake, fake, fake, ws, null) == 1
+    assert call(fake, fake, fake, fake, fake, fake, fake, fake, ws - 1, null) == 5
+    assert call(odd, fake, fake, fake, fake, fake, fake, fake, ws, null) == 4
+    assert call(fake, odd, fake, fake, fake, fake, fake, fake, ws, null) == 4
+    assert call(fake, fake, fake, fake, fake, fake, fake, odd, ws, null) == 4
+    # a plan for another shape is rejected
+    st2, p2 = plan(lib, 32, 512, 512, 16)
+    assert lib.spear_w4ec_linear(ctypes.byref(d), ctypes.byref(p2), fake, fake, fake, fake, fake, fake,
+                                 fake, fake, ws, null) == 6
+    bad = _binding.Plan.from_buffer_copy(p)
+    bad.grid += 1
+    assert lib.spear_w4ec_linear(ctypes.byref(d), ctypes.byref(bad), fake, fake, fake, fake, fake, fake,
+                                 fake, fake, ws, null) == 6
+    bad = _binding.Plan.from_buffer_copy(p)
+    bad.abi_version = 7
+    assert lib.spear_w4ec_linear(ctypes.byref(d), ctypes.byref(bad), fake, fake, fake, fake, fake, fake,
+                                 fake, fake, ws, null) == 6
+    # M = 0 is a no-op that succeeds without touching any pointer
+    d0 = _binding.LinearDesc(0, 512, 512, 16, 0.0, 0.0, 0, 256)
+    st0, p0 = plan(lib, 0, 512, 512, 16)
+    assert lib.spear_w4ec_linear(ctypes.byref(d0), ctypes.byref(p0), null, null, null, null, null, null,
+                                 null, null, 0, null) == 0
+
+
+def test_pack_and_unpack_checks(lib):
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(0)
+    assert lib.spear_pack_w4(null, 512, 512, fake, fake, null) == 1
+    assert lib.spear_pack_w4(fake, 500, 512, fake, fake, null) == 2
+    assert lib.spear_pack_w4(fake, 512, 512, ctypes.c_void_p(0x1004), fake, null) == 4
+    assert lib.spear_debug_unpack_w4(null, 512, 512, fake, null) == 1
+    assert lib.spear_debug_unpack_w4(fake, 8, 0, fake, null) == 2
+
+
+def test_ec_project_checks(lib):
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(0)
+    nb = ctypes.c_size_t(0)
+    assert lib.spear_ec_workspace_bytes(16, 512, 16, ctypes.byref(nb)) == 0 and nb.value > 0
+    assert lib.spear_ec_workspace_bytes(16, 512, 0, ctypes.byref(nb)) == 2
+    assert lib.spear_ec_project(16, 512, 16, fake, fake, fake, 0.0, 0.0, fake, fake, fake, 0, null) == 5
+    assert lib.spear_ec_project(16, 512, 16, null, fake, fake, 0.0, 0.0, fake, fake, fake, nb.value, null) == 1
+    assert lib.spear_ec_project(16, 512, 16, fake, fake, fake, float("nan"), 0.0, fake, fake, fake,
+                                nb.value, null) == 8

@@ -1,0 +1,192 @@
+// C ABI entry points (declared in include/spear_w4ec.h): argument checks,
+// planning, and launches.  Nothing here allocates device memory or
+// synchronizes; every check runs before anything is enqueued.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+
+using namespace spear;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_cache[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+spear_status_t device_cus(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPEAR_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (cached > 0) { *out = cached; return SPEAR_OK; }
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return SPEAR_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_cache[dev].store(cus, std::memory_order_relaxed);
+  *out = cus;
+  return SPEAR_OK;
+}
+
+spear_status_t plan_for(const spear_linear_desc_t& d, spear_plan_t* out) {
+  spear_status_t st = check_desc(d);
+  if (st != SPEAR_OK) return st;
+  int cus = d.device_cus;
+  if (cus == 0) {
+    st = device_cus(&cus);
+    if (st != SPEAR_OK) return st;
+  }
+  return make_plan(d, cus, out);
+}
+
+bool same_plan(const spear_plan_t& a, const spear_plan_t& b) {
+  return a.abi_version == b.abi_version && a.layout_id == b.layout_id && a.variant == b.variant &&
+         a.kernel == b.kernel && a.M == b.M && a.K == b.K && a.N == b.N && a.rank == b.rank &&
+         a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.split_k == b.split_k &&
+         a.grid == b.grid && a.producers == b.producers && a.ec_split == b.ec_split &&
+         a.cus == b.cus && a.workspace_bytes == b.workspace_bytes;
+}
+
+spear_status_t hip_status(hipError_t e) { return e == hipSuccess ? SPEAR_OK : SPEAR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* spear_status_str(spear_status_t s) {
+  switch (s) {
+    case SPEAR_OK: return "SPEAR_OK";
+    case SPEAR_ERR_NULL_POINTER: return "SPEAR_ERR_NULL_POINTER: a required pointer is NULL";
+    case SPEAR_ERR_INVALID_SHAPE: return "SPEAR_ERR_INVALID_SHAPE: need M >= 0, K >= 8, K % 8 == 0, N >= 1, 0 <= rank <= 256";
+    case SPEAR_ERR_UNSUPPORTED: return "SPEAR_ERR_UNSUPPORTED: request outside what the kernels implement";
+    case SPEAR_ERR_MISALIGNED: return "SPEAR_ERR_MISALIGNED: X, Wq and workspace need 16-byte, fp16 tensors 2-byte alignment";
+    case SPEAR_ERR_WORKSPACE_TOO_SMALL: return "SPEAR_ERR_WORKSPACE_TOO_SMALL: workspace_bytes < plan.workspace_bytes";
+    case SPEAR_ERR_INVALID_PLAN: return "SPEAR_ERR_INVALID_PLAN: plan does not match the descriptor or this library";
+    case SPEAR_ERR_HIP: return "SPEAR_ERR_HIP: the HIP runtime reported an error";
+    case SPEAR_ERR_INVALID_ARGUMENT: return "SPEAR_ERR_INVALID_ARGUMENT: non-finite bias, tau outside [0, 1] or unknown variant";
+  }
+  return "SPEAR_ERR_UNKNOWN";
+}
+
+uint32_t spear_abi_version(void) { return SPEAR_ABI_VERSION; }
+
+spear_status_t spear_packed_bytes(int32_t K, int32_t N, size_t* bytes) {
+  if (!bytes) return SPEAR_ERR_NULL_POINTER;
+  if (K < 8 || K % 8 != 0 || N < 1) return SPEAR_ERR_INVALID_SHAPE;
+  *bytes = (size_t)(k_pad(K) * n_pad(N) / 2);
+  return SPEAR_OK;
+}
+
+spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream) {
+  if (!W || !Wq || !scales) return SPEAR_ERR_NULL_POINTER;
+  if (K < 8 || K % 8 != 0 || N < 1) return SPEAR_ERR_INVALID_SHAPE;
+  if ((int64_t)K * 8 > INT32_MAX || (int64_t)N * 16 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
+  if (!aligned(W, 2) || !aligned(Wq, 16) || !aligned(scales, 2)) return SPEAR_ERR_MISALIGNED;
+  return hip_status(launch_pack_w4(W, K, N, Wq, scales, stream));
+}
+
+spear_status_t spear_debug_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream) {
+  if (!Wq || !q_out) return SPEAR_ERR_NULL_POINTER;
+  if (K < 8 || K % 8 != 0 || N < 1) return SPEAR_ERR_INVALID_SHAPE;
+  if (!aligned(Wq, 16)) return SPEAR_ERR_MISALIGNED;
+  return hip_status(launch_unpack_w4(Wq, K, N, q_out, stream));
+}
+
+spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t* plan) {
+  if (!desc || !plan) return SPEAR_ERR_NULL_POINTER;
+  return plan_for(*desc, plan);
+}
+
+spear_status_t spear_ec_workspace_bytes(int32_t M, int32_t K, int32_t rank, size_t* bytes) {
+  if (!bytes) return SPEAR_ERR_NULL_POINTER;
+  if (M < 0 || K < 8 || K % 8 != 0 || rank < 1 || rank > SPEAR_MAX_RANK) return SPEAR_ERR_INVALID_SHAPE;
+  *bytes = ec_workspace_layout(M, K, rank).bytes;
+  return SPEAR_OK;
+}
+
+spear_status_t spear_ec_project(int32_t M, int32_t K, int32_t rank, const void* X, const void* A,
+                                const void* w_g, float gate_bias, float skip_tau, void* P, void* g,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || K < 8 || K % 8 != 0 || rank < 1 || rank > SPEAR_MAX_RANK) return SPEAR_ERR_INVALID_SHAPE;
+  if (!std::isfinite(gate_bias) || !std::isfinite(skip_tau) || skip_tau < 0.0f || skip_tau > 1.0f)
+    return SPEAR_ERR_INVALID_ARGUMENT;
+  if (M == 0) return SPEAR_OK;
+  if (!X || !A || !w_g || !P || !g) return SPEAR_ERR_NULL_POINTER;
+  const EcWorkspace L = ec_workspace_layout(M, K, rank);
+  if (!workspace) return SPEAR_ERR_NULL_POINTER;
+  if (workspace_bytes < L.bytes) return SPEAR_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(X, 16) || !aligned(workspace, 16) || !aligned(A, 2) || !aligned(w_g, 2) ||
+      !aligned(P, 4) || !aligned(g, 4))
+    return SPEAR_ERR_MISALIGNED;
+  EcArgs e;
+  e.X = X; e.A = A; e.w_g = w_g;
+  e.M = M; e.K = K; e.rank = rank;
+  e.gate_bias = gate_bias; e.skip_tau = skip_tau;
+  e.workspace = workspace;
+  e.P_out = P; e.g_out = g; e.p_out_stride = rank;
+  return hip_status(launch_ec_project(e, stream));
+}
+
+spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_plan_t* plan,
+                                 const void* X, const void* Wq, const void* scales, const void* A,
+                                 const void* B, const void* w_g, void* Y, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!desc) return SPEAR_ERR_NULL_POINTER;
+  spear_status_t st = check_desc(*desc);
+  if (st != SPEAR_OK) return st;
+  spear_plan_t p;
+  if (plan) {
+    if (plan->abi_version != SPEAR_ABI_VERSION || plan->layout_id != SPEAR_LAYOUT_ID)
+      return SPEAR_ERR_INVALID_PLAN;
+    if (plan->variant < SPEAR_VARIANT_FUSED || plan->variant > SPEAR_VARIANT_NO_EC || plan->cus <= 0)
+      return SPEAR_ERR_INVALID_PLAN;
+    spear_linear_desc_t d2 = *desc;
+    d2.variant = plan->variant;
+    d2.device_cus = plan->cus;
+    spear_plan_t again;
+    st = make_plan(d2, plan->cus, &again);
+    if (st != SPEAR_OK || !same_plan(again, *plan)) return SPEAR_ERR_INVALID_PLAN;
+    p = *plan;
+  } else {
+    st = plan_for(*desc, &p);
+    if (st != SPEAR_OK) return st;
+  }
+  if (desc->M == 0) return SPEAR_OK;
+  const bool ec = p.variant != SPEAR_VARIANT_NO_EC;
+  if (!X || !Wq || !scales || !Y) return SPEAR_ERR_NULL_POINTER;
+  if (ec && (!A || !B || !w_g)) return SPEAR_ERR_NULL_POINTER;
+  if (p.workspace_bytes > 0 && !workspace) return SPEAR_ERR_NULL_POINTER;
+  if (workspace_bytes < p.workspace_bytes) return SPEAR_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(X, 16) || !aligned(Wq, 16) || !aligned(scales, 2) || !aligned(Y, 2))
+    return SPEAR_ERR_MISALIGNED;
+  if (workspace && !aligned(workspace, 16)) return SPEAR_ERR_MISALIGNED;
+  if (ec && (!aligned(A, 2) || !aligned(B, 2) || !aligned(w_g, 2))) return SPEAR_ERR_MISALIGNED;
+
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.X = X; ga.Wq = Wq; ga.scales = scales; ga.Y = Y;
+  ga.M = desc->M; ga.K = desc->K; ga.N = desc->N; ga.rank = desc->rank;
+  if (ec) {
+    const EcWorkspace L = ec_workspace_layout(desc->M, desc->K, desc->rank);
+    EcArgs e;
+    e.X = X; e.A = A; e.w_g = w_g;
+    e.M = desc->M; e.K = desc->K; e.rank = desc->rank;
+    e.gate_bias = desc->gate_bias; e.skip_tau = desc->skip_tau;
+    e.workspace = workspace;
+    e.P_out = nullptr; e.g_out = nullptr; e.p_out_stride = 0;
+    st = hip_status(launch_ec_project(e, stream));
+    if (st != SPEAR_OK) return st;
+    ga.B = B;
+    ga.P = (const float*)((const char*)workspace + L.p);
+    ga.g = (const float*)((const char*)workspace + L.g);
+    ga.ec = 1;
+  }
+  return hip_status(launch_gemm(ga, p, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Device helpers shared by the gfx950 kernels of the W4+EC linear layer.
+//
+// Matrix instruction: v_mfma_f32_16x16x32_f16 (64 lanes).  For lane L,
+// t = L / 16 and c = L % 16:
+//   A operand (16 x 32): row c, k = 8t .. 8t+7 (8 halves, 16 bytes)
+//   B operand (32 x 16): column c, k = 8t .. 8t+7
+//   C/D (16 x 16 fp32): column c, rows 4t .. 4t+3
+// The packed weight (layout id 2) stores, in the 16 bytes of lane slot L of
+// every 1 KiB tile, the B operand of that lane for four consecutive 32-k
+// blocks, so one 16-byte load per lane feeds four instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spear {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kKChunk = 128;   // k extent of one packed tile
+constexpr int kNBlock = 16;    // columns of one packed panel
+constexpr uint32_t kZeroCodeWord = 0x88888888u;  // eight codes u = 8 (q = 0)
+
+__device__ __forceinline__ float4_t mfma16x16x32(const half8_t& a, const half8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Decode one packed word (eight 4-bit codes u, fields in k order
+// 0,2,4,6,1,3,5,7) into the eight fp16 values q = u - 8 in k order.
+// OR-ing 0x6400 into a 16-bit half holding u (< 16) in its low mantissa bits
+// gives exactly the fp16 value 1024 + u; subtracting 1032 leaves u - 8.
+__device__ __forceinline__ half8_t decode_w4(uint32_t w) {
+  const uint32_t m = 0x000F000Fu, e = 0x64006400u;
+  const uint32_t d0 = (w & m) | e;
+  const uint32_t d1 = ((w >> 4) & m) | e;
+  const uint32_t d2 = ((w >> 8) & m) | e;
+  const uint32_t d3 = ((w >> 12) & m) | e;
+  const half2_t bias = {(half_t)1032.0f, (half_t)1032.0f};
+  const half2_t h0 = __builtin_bit_cast(half2_t, d0) - bias;
+  const half2_t h1 = __builtin_bit_cast(half2_t, d1) - bias;
+  const half2_t h2 = __builtin_bit_cast(half2_t, d2) - bias;
+  const half2_t h3 = __builtin_bit_cast(half2_t, d3) - bias;
+  half8_t r;
+  r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
+  r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
+  return r;
+}
+
+__device__ __forceinline__ half8_t zero_half8() {
+  half8_t z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (half_t)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ float4_t zero_float4() {
+  float4_t z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// 16-byte load of 8 halves; the caller guarantees 16-byte alignment.
+__device__ __forceinline__ half8_t load_half8(const half_t* p) {
+  return *reinterpret_cast<const half8_t*>(p);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+}  // namespace spear

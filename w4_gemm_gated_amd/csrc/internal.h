@@ -1,0 +1,81 @@
+// Internal interfaces between the C ABI (api.cpp), the host planner
+// (plan.cpp) and the kernel launchers (*.hip).  Not installed; not part of
+// the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/spear_w4ec.h"
+
+namespace spear {
+
+// ----------------------------------------------------------------- geometry
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+inline int64_t k_pad(int64_t K) { return round_up(K, 128); }
+inline int64_t n_pad(int64_t N) { return round_up(N, 16); }
+
+// Columns of the EC projection output: rank columns of P, one of the gate
+// logit, padded to the 16-column granule of the matrix instruction.
+inline int64_t ec_cols(int64_t rank) { return round_up(rank + 1, 16); }
+// Row stride (floats) of the stored P: rank padded to the 32-k granule.
+inline int64_t p_stride(int64_t rank) { return round_up(rank, 32); }
+
+// Workspace layout of the EC projection (offsets in bytes, 256-aligned).
+struct EcWorkspace {
+  int32_t m_tiles = 0;   // row tiles of the projection
+  int32_t tile_rows = 0; // rows per tile (16 or 64)
+  int32_t splits = 0;    // K slices
+  int32_t k_slice = 0;   // k per slice (multiple of 32)
+  size_t counters = 0;   // uint32 [m_tiles]
+  size_t partials = 0;   // float [splits][m_tiles * tile_rows][ec_cols]
+  size_t p = 0;          // float [M][p_stride]
+  size_t g = 0;          // float [M]
+  size_t bytes = 0;
+};
+EcWorkspace ec_workspace_layout(int64_t M, int64_t K, int64_t rank);
+
+// Host planner (pure host code; no HIP calls).
+spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* plan);
+spear_status_t check_desc(const spear_linear_desc_t& d);
+
+// Shapes of the main kernel families.
+constexpr int kSkinnyMaxM = 16;   // rows handled by the skinny kernel
+
+// ----------------------------------------------------------------- launchers
+
+struct EcArgs {
+  const void* X;      // fp16 [M, K]
+  const void* A;      // fp16 [K, rank]
+  const void* w_g;    // fp16 [K]
+  int32_t M, K, rank;
+  float gate_bias, skip_tau;
+  void* workspace;    // base; layout from ec_workspace_layout
+  void* P_out;        // float [M][p_stride] (may alias workspace P)
+  void* g_out;        // float [M]
+  int32_t p_out_stride;  // floats per row of P_out
+};
+
+struct GemmArgs {
+  const void* X;       // fp16 [M, K]
+  const void* Wq;      // packed, layout id 2
+  const void* scales;  // fp16 [N]
+  const void* B;       // fp16 [rank, N] (EC) or null
+  const float* P;      // float [M][p_stride] or null
+  const float* g;      // float [M] or null
+  void* Y;             // fp16 [M, N]
+  int32_t M, K, N, rank;
+  int32_t ec;          // apply the gated EC term
+};
+
+hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
+hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);
+hipError_t launch_ec_project(const EcArgs& a, void* stream);
+hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream);
+
+}  // namespace spear

@@ -1,0 +1,70 @@
+// Host planner: the adaptive kernel-fusion dispatch of the SPEAR abstract,
+// reduced to what one GPU needs.  Pure host arithmetic on the descriptor; the
+// device is touched only by the caller (api.cpp) to read the CU count.
+//
+// Decisions:
+//   * no EC (rank 0) or variant NO_EC            -> NO_EC: the W4 GEMM alone;
+//   * AUTO                                       -> SPLIT (EC projection
+//     launch, then the GEMM with the gated epilogue);
+//   * the per-token gate-value decision (skip the EC term where every gate of
+//     a wave's rows is below tau) is taken on the device in the epilogue.
+//   * main kernel family by M: skinny (M <= 16 rows, K split over the four
+//     waves of a workgroup) or tiled (128 x 128 tiles).
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+
+namespace spear {
+
+spear_status_t check_desc(const spear_linear_desc_t& d) {
+  if (d.M < 0 || d.K < 8 || d.K % 8 != 0 || d.N < 1) return SPEAR_ERR_INVALID_SHAPE;
+  if (d.rank < 0 || d.rank > SPEAR_MAX_RANK) return SPEAR_ERR_INVALID_SHAPE;
+  if (d.variant < SPEAR_VARIANT_AUTO || d.variant > SPEAR_VARIANT_NO_EC) return SPEAR_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(d.gate_bias) || !std::isfinite(d.skip_tau)) return SPEAR_ERR_INVALID_ARGUMENT;
+  if (d.skip_tau < 0.0f || d.skip_tau > 1.0f) return SPEAR_ERR_INVALID_ARGUMENT;
+  if (d.device_cus < 0) return SPEAR_ERR_INVALID_ARGUMENT;
+  // Index arithmetic inside the kernels uses 32-bit row and column counts.
+  if ((int64_t)d.K * 8 > INT32_MAX || (int64_t)d.N * 16 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
+  return SPEAR_OK;
+}
+
+spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* plan) {
+  const spear_status_t st = check_desc(d);
+  if (st != SPEAR_OK) return st;
+  spear_plan_t p;
+  std::memset(&p, 0, sizeof(p));
+  p.abi_version = SPEAR_ABI_VERSION;
+  p.layout_id = SPEAR_LAYOUT_ID;
+  p.M = d.M; p.K = d.K; p.N = d.N; p.rank = d.rank;
+  p.cus = cus;
+  const bool ec = d.rank > 0 && d.variant != SPEAR_VARIANT_NO_EC;
+  if (!ec) {
+    p.variant = SPEAR_VARIANT_NO_EC;
+  } else if (d.variant == SPEAR_VARIANT_FUSED) {
+    return SPEAR_ERR_UNSUPPORTED;
+  } else {
+    p.variant = SPEAR_VARIANT_SPLIT;
+  }
+  const int64_t nblk = n_pad(d.N) / 16;
+  if (d.M <= kSkinnyMaxM) {
+    p.kernel = 0;
+    p.tile_m = 16; p.tile_n = 16;
+    p.grid = (int32_t)(nblk * ceil_div(d.M, 16));
+  } else {
+    p.kernel = 1;
+    p.tile_m = 128; p.tile_n = 128;
+    p.grid = (int32_t)(ceil_div(nblk, 8) * ceil_div(d.M, 128));
+  }
+  p.split_k = 1;
+  if (p.variant == SPEAR_VARIANT_SPLIT) {
+    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank);
+    p.producers = L.m_tiles * L.splits;
+    p.ec_split = L.splits;
+    p.workspace_bytes = L.bytes;
+  }
+  *plan = p;
+  return SPEAR_OK;
+}
+
+}  // namespace spear
