@@ -1,0 +1,270 @@
+"""Benchmark of the W4+EC linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: decode, Llama-3-8B q_proj shape (K = N = 4096, EC rank 32,
+gate bias -1, 1% outlier input channels x20), token counts M = 1, 4 and 16.
+One step = one call of the layer (EC projection and gate, W4 GEMM, gated EC
+epilogue) for each of the three token counts.  `value` is HBM GB/s: the
+algorithmic bytes of the three calls (packed weight, scales, X, Y, A, B, w_g)
+over their measured time, inputs resident in HBM, weights cold: every call
+reads one of R copies of the weights, R x bytes >= 512 MiB (twice the
+last-level cache).  Timing uses HIP events on the stream the library launches
+on (torch's current stream).
+
+Also reported on the same line: per-token-count times and the EC overhead
+(same calls with the EC switched off), the prefill workload (M = 2048,
+K = 4096, N = 14336, rank 64) in TFLOP/s against the fp16 matrix-core peak,
+and the fp64 oracle timed on the host cores on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_FP16_PEAK_TFS = 2500.0    # MI355X dense fp16 matrix cores, published
+COLD_BYTES = 512 << 20
+METRIC = "W4+EC linear TFLOP/s and HBM GB/s (% roofline) at decode M=1–16 and prefill M=2048"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=30)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Layer:
+    """R device copies of one layer's weights (same values, distinct addresses)."""
+
+    def __init__(self, torch, sp, w, copies):
+        dev = "cuda:0"
+        t = lambda a: None if a is None else torch.from_numpy(a).to(dev)  # noqa: E731
+        W = t(w["W"])
+        Wq, s = sp.spear_pack_w4(W)
+        del W
+        A, B, wg = t(w["A"]), t(w["B"]), t(w["w_g"])
+        self.sets = []
+        for i in range(copies):
+            if i == 0:
+                self.sets.append((Wq, s, A, B, wg))
+            else:
+                self.sets.append(tuple(x.clone() for x in (Wq, s, A, B, wg)))
+        self.X = t(w["X"])
+        self.K, self.N, self.r = w["K"], w["N"], w["r"]
+
+
+def time_calls(torch, calls, steps, warmup, graph=True):
+    """calls: list of callables forming one step.  Returns seconds per step,
+    measured with events on the current stream.  With graph=True the steps
+    are captured once into a HIP graph and the graph is replayed, so the
+    figure is the GPU's back-to-back rate, free of Python launch overhead."""
+    for i in range(warmup):
+        for c in calls:
+            c(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    for c in calls:
+                        c(warmup + i)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()                       # one untimed replay
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        del g
+    else:
+        start.record()
+        for i in range(steps):
+            for c in calls:
+                c(warmup + i)
+        stop.record()
+        torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / steps
+
+
+def make_call(sp, layer, M, b_g, variant, Ys, plans, workspace):
+    plan = plans[(M, variant)]
+    X = layer.X[:M]
+
+    def call(i):
+        Wq, s, A, B, wg = layer.sets[i % len(layer.sets)]
+        if variant == "no_ec":
+            A = B = wg = None
+        sp.spear_w4ec_linear(X, Wq, s, A, B, wg, b_g, 0.0, variant, N=layer.N, plan=plan,
+                             Y=Ys[i % len(Ys)][:M], workspace=workspace)
+    return call
+
+
+def cpu_baseline(w, ms, budget_s):
+    """The oracle as it stands, on a bounded sample of the decode step."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()}))
+    except Exception:  # noqa: BLE001 - informational only
+        threads, blas = os.cpu_count() or 1, "?"
+    Wq, s = oracle.pack_w4(w["W"])
+    t0 = time.perf_counter()
+    steps, nbytes = 0, 0
+    while True:
+        for M in ms:
+            oracle.w4ec_linear(w["X"][:M], Wq, s, w["A"], w["B"], w["w_g"], w["b_g"][M], K=w["K"], N=w["N"])
+            nbytes += workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 20:
+            break
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{steps} decode step(s) (M=1,4,16 on K=N=4096, r=32), numpy float64 oracle incl. "
+                      f"dequantizing the packed weight each call, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this layer runs on a "
+              "single GPU; multi-GPU sharding is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import w4_gemm_gated_amd as sp
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    sp.library()
+
+    # ------------------------------------------------------------ decode
+    w = workloads.workload(2)
+    ms = w["ms"]
+    per_set = workloads.algorithmic_bytes(16, w["K"], w["N"], w["r"])
+    copies = max(2, -(-COLD_BYTES // per_set))
+    log(f"decode: K=N=4096 r=32, {copies} weight copies")
+    dec = Layer(torch, sp, w, copies)
+    Ys = [torch.empty((16, w["N"]), dtype=torch.float16, device="cuda:0") for _ in range(8)]
+    plans = {}
+    for M in ms:
+        for v in ("auto", "no_ec"):
+            plans[(M, v)] = sp.spear_dispatch_plan(M, w["K"], w["N"], w["r"] if v == "auto" else 0,
+                                                   w["b_g"][M], 0.0, v)
+    ws_bytes = max(p.workspace_bytes for p in plans.values())
+    ws = torch.zeros(max(ws_bytes, 1 << 20), dtype=torch.uint8, device="cuda:0")
+    graph = not args.eager
+    step_calls = [make_call(sp, dec, M, w["b_g"][M], "auto", Ys, plans, ws) for M in ms]
+    t_step = time_calls(torch, step_calls, args.steps, args.warmup, graph)
+    step_bytes = sum(workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"]) for M in ms)
+    value = step_bytes / t_step / 1e9
+    per_m, overhead = {}, {}
+    for M in ms:
+        b = workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"])
+        t_on = time_calls(torch, [make_call(sp, dec, M, w["b_g"][M], "auto", Ys, plans, ws)], args.steps,
+                          args.warmup, graph)
+        t_off = time_calls(torch, [make_call(sp, dec, M, 0.0, "no_ec", Ys, plans, ws)], args.steps,
+                           args.warmup, graph)
+        b_off = workloads.algorithmic_bytes(M, w["K"], w["N"], 0)
+        per_m[str(M)] = {"us": round(t_on * 1e6, 3), "GB/s": round(b / t_on / 1e9, 1),
+                         "frac_hbm": round(b / t_on / 1e9 / HBM_PEAK_GBS, 4),
+                         "variant": _binding_variant(plans[(M, "auto")]),
+                         "no_ec_us": round(t_off * 1e6, 3), "no_ec_GB/s": round(b_off / t_off / 1e9, 1)}
+        overhead[str(M)] = round(t_on / t_off - 1.0, 4)
+        log(f"decode M={M}: {t_on * 1e6:.2f} us ({b / t_on / 1e9:.0f} GB/s), EC off {t_off * 1e6:.2f} us")
+    dom_m = "16"
+    b16 = workloads.algorithmic_bytes(16, w["K"], w["N"], w["r"])
+    achieved = b16 / (per_m[dom_m]["us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode call at M=16 (all launches of one call)",
+                "bytes_per_launch": b16}
+    del dec
+
+    # ------------------------------------------------------------ prefill
+    prefill = None
+    if not args.no_prefill:
+        wp = workloads.workload(3)
+        pb = workloads.algorithmic_bytes(2048, wp["K"], wp["N"], wp["r"])
+        pcopies = max(2, -(-COLD_BYTES // pb))
+        log(f"prefill: M=2048 K=4096 N=14336 r=64, {pcopies} weight copies")
+        pre = Layer(torch, sp, wp, pcopies)
+        pYs = [torch.empty((2048, wp["N"]), dtype=torch.float16, device="cuda:0") for _ in range(2)]
+        pplans = {(2048, "auto"): sp.spear_dispatch_plan(2048, wp["K"], wp["N"], wp["r"], 0.0, 0.0, "auto"),
+                  (2048, "no_ec"): sp.spear_dispatch_plan(2048, wp["K"], wp["N"], 0, 0.0, 0.0, "no_ec")}
+        pws = torch.zeros(max(max(p.workspace_bytes for p in pplans.values()), 1 << 20), dtype=torch.uint8,
+                          device="cuda:0")
+        t_on = time_calls(torch, [make_call(sp, pre, 2048, 0.0, "auto", pYs, pplans, pws)], args.prefill_steps, 3,
+                          graph)
+        t_off = time_calls(torch, [make_call(sp, pre, 2048, 0.0, "no_ec", pYs, pplans, pws)], args.prefill_steps,
+                           3, graph)
+        main_f, ec_f = workloads.algorithmic_flops(2048, wp["K"], wp["N"], wp["r"])
+        tf = main_f / t_on / 1e12
+        prefill = {"us": round(t_on * 1e6, 2), "TFLOP/s": round(tf, 1),
+                   "frac_mfma_fp16": round(tf / MFMA_FP16_PEAK_TFS, 4),
+                   "TFLOP/s_incl_ec": round((main_f + ec_f) / t_on / 1e12, 1),
+                   "no_ec_us": round(t_off * 1e6, 2), "ec_overhead": round(t_on / t_off - 1.0, 4),
+                   "variant": _binding_variant(pplans[(2048, "auto")])}
+        log(f"prefill: {t_on * 1e6:.1f} us, {tf:.1f} TFLOP/s; EC off {t_off * 1e6:.1f} us")
+        del pre, pYs
+
+    # ------------------------------------------------------------ oracle on the host
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(w, ms, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "timing": "hip graph replay of back-to-back calls" if graph else "eager launches",
+        "data": "synthetic",
+        "config": {"workload": "decode q_proj 4096x4096, W4 per-channel + EC rank 32, gate bias -1, "
+                               "1% outlier channels x20, M=1,4,16 per step, cold weights",
+                   "K": w["K"], "N": w["N"], "rank": w["r"], "tokens": list(ms), "weight_copies": copies},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_m": per_m,
+        "ec_overhead": overhead,
+        "prefill": prefill,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _binding_variant(plan):
+    return {1: "fused", 2: "split", 3: "no_ec"}.get(plan.variant, "?")
+
+
+if __name__ == "__main__":
+    main()

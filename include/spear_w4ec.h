@@ -140,17 +140,19 @@ spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t
  *            spear_dispatch_plan for the same M, K, N, rank and variant.
  *   X        fp16 [M, K], 16-byte aligned.
  *   Wq, scales  from spear_pack_w4 (16- and 2-byte aligned).
- *   A        fp16 [K, rank], B fp16 [rank, N], w_g fp16 [K] (2-byte aligned);
- *            may be NULL when rank == 0 or the resolved variant is NO_EC.
+ *   A        fp16 [K, rank], B fp16 [rank, N], w_g fp16 [K] (2-byte aligned;
+ *            A and w_g 16-byte aligned for the fused variant); may be NULL when
+ *            rank == 0 or the resolved variant is NO_EC.  Inputs must be finite.
  *   Y        output fp16 [M, N] (2-byte aligned), fully overwritten,
  *            fp16(s[n] acc[m,n] + g'[m] sum_j P[m,j] B[j,n]) with fp32
  *            accumulation; must not alias any input.
  *   workspace  device memory of at least plan.workspace_bytes (16-byte
  *            aligned; may be NULL when that is 0).  It must be zero-filled
- *            before its first use.  Its leading bytes hold the cross-
- *            workgroup counters, which every call returns to zero; the rest
- *            is scratch, so a workspace can be reused without clearing.
- *            Calls that run concurrently must not share a workspace.
+ *            before its first use.  Its first 64 KiB hold cross-workgroup
+ *            counters, which every call returns to zero; the rest is
+ *            scratch.  So a zero-filled workspace can be reused, without
+ *            clearing, by later calls of any plan that fit in it.  Calls
+ *            that run concurrently must not share a workspace.
  * Errors: NULL_POINTER, INVALID_SHAPE, INVALID_ARGUMENT, MISALIGNED,
  *         WORKSPACE_TOO_SMALL, INVALID_PLAN, UNSUPPORTED, HIP.
  */

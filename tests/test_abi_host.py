@@ -69,8 +69,14 @@ def test_dispatch_rules(lib):
     assert st == 0 and p.variant in (1, 2) and p.kernel == 0 and p.workspace_bytes > 0
     st, p = plan(lib, 2048, 4096, 14336, 64)
     assert st == 0 and p.variant == 2 and p.kernel == 1 and p.workspace_bytes > 0
+    st, p = plan(lib, 16, 4096, 4096, 32)
+    assert p.variant == 1 and p.producers > 0 and p.grid > p.producers
     st, p = plan(lib, 16, 4096, 4096, 0)
-    assert st == 0 and p.variant == 3 and p.workspace_bytes == 0
+    assert st == 0 and p.variant == 3 and p.producers == 0
+    st, p = plan(lib, 16, 4096, 4096, 32, variant=2)
+    assert st == 0 and p.variant == 2
+    st, p = plan(lib, 64, 4096, 4096, 32, variant=1)
+    assert st == 3                        # the fused variant is built for M <= 16
     st, p = plan(lib, 64, 4096, 4096, 32, variant=3)
     assert st == 0 and p.variant == 3 and p.workspace_bytes == 0
     st, p = plan(lib, 0, 512, 512, 16)

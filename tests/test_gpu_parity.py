@@ -214,5 +214,15 @@ def test_repeat_calls_deterministic_and_workspace_clean():
     Y2 = sp.spear_w4ec_linear(*args, plan=p, workspace=ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
-    # counters are back at zero (the rest of the workspace is scratch)
-    assert int(ws[:256].view(torch.int32).abs().sum().item()) == 0
+    # the 64 KiB counter header is back at zero; the rest is scratch
+    assert int(ws[: 64 * 1024].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("variant", ["fused", "split", "no_ec"])
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_skinny_variants_agree(variant, M):
+    """Every variant of the skinny path against the oracle (decode shape)."""
+    w = workloads.workload(2)
+    X = np.ascontiguousarray(np.concatenate([w["X"], w["X"]])[:M])
+    A, B, w_g = (w["A"], w["B"], w["w_g"]) if variant != "no_ec" else (None, None, None)
+    layer_case(X, w["W"], A, B, w_g, -1.0, 0.0, variant, f"skinny {variant} M={M}")

@@ -166,13 +166,14 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
     return SPEAR_ERR_MISALIGNED;
   if (workspace && !aligned(workspace, 16)) return SPEAR_ERR_MISALIGNED;
   if (ec && (!aligned(A, 2) || !aligned(B, 2) || !aligned(w_g, 2))) return SPEAR_ERR_MISALIGNED;
+  if (p.variant == SPEAR_VARIANT_FUSED && (!aligned(A, 16) || !aligned(w_g, 16))) return SPEAR_ERR_MISALIGNED;
 
-  GemmArgs ga;
-  std::memset(&ga, 0, sizeof(ga));
-  ga.X = X; ga.Wq = Wq; ga.scales = scales; ga.Y = Y;
-  ga.M = desc->M; ga.K = desc->K; ga.N = desc->N; ga.rank = desc->rank;
-  if (ec) {
-    const EcWorkspace L = ec_workspace_layout(desc->M, desc->K, desc->rank);
+  const bool skinny = p.kernel == 0;
+  size_t ec_bytes = 0;
+  EcWorkspace L;
+  if (p.variant == SPEAR_VARIANT_SPLIT) {
+    L = ec_workspace_layout(desc->M, desc->K, desc->rank);
+    ec_bytes = L.bytes;
     EcArgs e;
     e.X = X; e.A = A; e.w_g = w_g;
     e.M = desc->M; e.K = desc->K; e.rank = desc->rank;
@@ -181,6 +182,25 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
     e.P_out = nullptr; e.g_out = nullptr; e.p_out_stride = 0;
     st = hip_status(launch_ec_project(e, stream));
     if (st != SPEAR_OK) return st;
+  }
+  if (skinny) {
+    SkinnyLaunch s;
+    s.shape = skinny_shape(desc->M, desc->K, desc->N, desc->rank, p.variant == SPEAR_VARIANT_FUSED, p.cus,
+                           ec_bytes ? ec_bytes : kSyncHeaderBytes);
+    s.X = X; s.Wq = Wq; s.scales = scales; s.A = A; s.B = B; s.w_g = w_g; s.Y = Y;
+    s.M = desc->M; s.K = desc->K; s.N = desc->N; s.rank = ec ? desc->rank : 0;
+    s.ec_mode = p.variant == SPEAR_VARIANT_FUSED ? 1 : (p.variant == SPEAR_VARIANT_SPLIT ? 2 : 0);
+    s.gate_bias = desc->gate_bias; s.skip_tau = desc->skip_tau;
+    s.workspace = workspace;
+    s.Pext = ec_bytes ? (const float*)((const char*)workspace + L.p) : nullptr;
+    s.gext = ec_bytes ? (const float*)((const char*)workspace + L.g) : nullptr;
+    return hip_status(launch_skinny(s, stream));
+  }
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.X = X; ga.Wq = Wq; ga.scales = scales; ga.Y = Y;
+  ga.M = desc->M; ga.K = desc->K; ga.N = desc->N; ga.rank = desc->rank;
+  if (ec) {
     ga.B = B;
     ga.P = (const float*)((const char*)workspace + L.p);
     ga.g = (const float*)((const char*)workspace + L.g);

@@ -70,4 +70,44 @@ __device__ __forceinline__ half8_t load_half8(const half_t* p) {
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// Buffer resource over [base, base + bytes): raw buffer loads at an offset
+// outside it return zeros without touching memory, which masks lanes without
+// a branch (a branch around a load makes the compiler wait for it early).
+constexpr uint32_t kBufferRsrcWord3 = 0x00020000u;   // gfx9 family: 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;         // offset beyond any resource here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufferRsrcWord3);
+}
+__device__ __forceinline__ half8_t buffer_load_half8(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset) {
+  return __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup exchange without L2 write-backs.  Workgroups on different
+// XCDs do not share an L2, and a release/acquire fence at device scope
+// writes back / invalidates the whole L2 of the issuing XCD.  Data exchanged
+// between workgroups is instead stored and loaded with device-scope relaxed
+// atomics, which the compiler emits as sc1 (device-coherent) stores and
+// loads; the writer drains its stores (s_waitcnt vmcnt(0)) before it bumps
+// the device-scope counter that publishes them, and the reader loads the data
+// only after it has seen the counter (or flag).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev_u32(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory instruction this wave issued has completed.
+__device__ __forceinline__ void drain_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace spear

@@ -6,9 +6,10 @@
 //
 // The K dimension is cut into slices; each workgroup computes one
 // (row tile, K slice) partial and stores it in the workspace.  The last
-// workgroup of a row tile to finish (a device-scope counter) adds the slices
-// in fixed order, so the result does not depend on scheduling, applies the
-// gate, writes P and g', and resets the counter.
+// workgroup of a row tile to finish (a device-scope counter; partials move
+// through device-coherent stores and loads) adds the slices in fixed order,
+// so the result does not depend on scheduling, applies the gate, writes P and
+// g', and resets the counter.
 #include "device_common.h"
 #include "internal.h"
 
@@ -22,9 +23,9 @@ EcWorkspace ec_workspace_layout(int64_t M, int64_t K, int64_t rank) {
   w.k_slice = 256;
   w.splits = (int32_t)ceil_div(K, w.k_slice);
   const int64_t cols = ec_cols(rank);
-  size_t off = 0;
+  size_t off = kSyncHeaderBytes;
   auto take = [&](size_t bytes) { size_t o = off; off = (size_t)round_up((int64_t)(off + bytes), 256); return o; };
-  w.counters = take(sizeof(uint32_t) * (size_t)w.m_tiles);
+  w.counters = 0;   // in the counter header
   w.partials = take(sizeof(float) * (size_t)w.splits * (size_t)w.m_tiles * w.tile_rows * cols);
   w.p = take(sizeof(float) * (size_t)M * (size_t)p_stride(rank));
   w.g = take(sizeof(float) * (size_t)M);
@@ -104,18 +105,17 @@ __global__ void __launch_bounds__(kEcThreads) ec_project_kernel(EcKArgs a) {
       const int lr0 = (WM == 4 ? wave * 16 : 0) + 4 * t;
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        a.partials[(part_base + lr0 + v) * a.cols + nb * 16 + c16] = acc[nb][v];
+        st_dev(&a.partials[(part_base + lr0 + v) * a.cols + nb * 16 + c16], acc[nb][v]);
     }
   }
-  __threadfence();
+  drain_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[m_tile], 1u);
+    const uint32_t prev = add_dev_u32(&a.counters[m_tile], 1u);
     last_flag = (prev == (uint32_t)(a.splits - 1)) ? 1u : 0u;
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
 
   // Last arriver: fixed-order sum over the slices, gate, publish.
   const int rows_here = min(a.tile_rows, a.M - m_tile * a.tile_rows);
@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(kEcThreads) ec_project_kernel(EcKArgs a) {
     if (c > a.rank) continue;
     float s = 0.0f;
     for (int sp = 0; sp < a.splits; ++sp)
-      s += a.partials[(((size_t)sp * a.m_tiles + m_tile) * a.tile_rows + lr) * a.cols + c];
+      s += ld_dev(&a.partials[(((size_t)sp * a.m_tiles + m_tile) * a.tile_rows + lr) * a.cols + c]);
     const int row = m_tile * a.tile_rows + lr;
     if (c < a.rank) {
       a.P_out[(size_t)row * a.p_out_stride + c] = s;
@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(kEcThreads) ec_project_kernel(EcKArgs a) {
       a.P_out[(size_t)(m_tile * a.tile_rows + lr) * a.p_out_stride + c] = 0.0f;
     }
   }
-  if (threadIdx.x == 0) a.counters[m_tile] = 0u;
+  if (threadIdx.x == 0) st_dev_u32(&a.counters[m_tile], 0u);
 }
 
 }  // namespace

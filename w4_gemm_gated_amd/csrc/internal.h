@@ -26,6 +26,15 @@ inline int64_t ec_cols(int64_t rank) { return round_up(rank + 1, 16); }
 // Row stride (floats) of the stored P: rank padded to the 32-k granule.
 inline int64_t p_stride(int64_t rank) { return round_up(rank, 32); }
 
+// Every workspace starts with a fixed 64 KiB header of cross-workgroup
+// counters, which every call returns to zero: EC-projection counters in the
+// first half, GEMM counters in the second.  All scratch lies after it, so a
+// zero-filled workspace serves calls of any plan (each plan's counters sit
+// in the header, never in another plan's scratch).
+constexpr size_t kSyncHeaderBytes = 64 * 1024;
+constexpr size_t kGemmSyncOffset = 32 * 1024;
+constexpr int64_t kMaxSyncWords = 8192;   // per half of the header
+
 // Workspace layout of the EC projection (offsets in bytes, 256-aligned).
 struct EcWorkspace {
   int32_t m_tiles = 0;   // row tiles of the projection
@@ -72,6 +81,43 @@ struct GemmArgs {
   int32_t M, K, N, rank;
   int32_t ec;          // apply the gated EC term
 };
+
+// Skinny (M <= 16) kernel: tile shape, producers and workspace layout.
+struct SkinnyShape {
+  int nbw = 1;      // 16-column panels per workgroup
+  int S = 1;        // K splits across workgroups
+  int T = 0;        // column tiles
+  int CPS = 0;      // 128-k chunks per split
+  int CPW = 1;      // chunks per wave (<= 4)
+  int P = 0;        // EC producer workgroups (fused variant)
+  int ksp = 0;      // k per producer slab
+  size_t lds = 0;   // dynamic LDS of a producer
+  size_t lds_gemm = 0;  // dynamic LDS of a GEMM workgroup (EC factor tile)
+  size_t ws_sync = 0, ws_ec_part = 0, ws_ec_final = 0, ws_gemm_part = 0;
+  size_t ws_bytes = 0;   // total workspace (0: none needed)
+  bool sync_ok = true;   // the tile counters fit the counter header
+};
+// scratch_base: first byte of the workspace this kernel may use as scratch.
+SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fused, int cus,
+                         size_t scratch_base);
+
+struct SkinnyLaunch {
+  SkinnyShape shape;
+  const void* X;
+  const void* Wq;
+  const void* scales;
+  const void* A;
+  const void* B;
+  const void* w_g;
+  void* Y;
+  int32_t M, K, N, rank;
+  int32_t ec_mode;          // 0 none, 1 fused, 2 P/g given
+  float gate_bias, skip_tau;
+  void* workspace;          // skinny workspace (layout in shape)
+  const float* Pext;        // ec_mode 2
+  const float* gext;
+};
+hipError_t launch_skinny(const SkinnyLaunch& L, void* stream);
 
 hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);

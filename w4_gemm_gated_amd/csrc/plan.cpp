@@ -4,8 +4,10 @@
 //
 // Decisions:
 //   * no EC (rank 0) or variant NO_EC            -> NO_EC: the W4 GEMM alone;
-//   * AUTO                                       -> SPLIT (EC projection
-//     launch, then the GEMM with the gated epilogue);
+//   * AUTO, M <= 16 rows                         -> FUSED: one launch (EC
+//     producers, split-K W4 GEMM, gated epilogue);
+//   * AUTO, M > 16                               -> SPLIT (EC projection
+//     launch, then the tiled GEMM with the gated epilogue);
 //   * the per-token gate-value decision (skip the EC term where every gate of
 //     a wave's rows is below tau) is taken on the device in the epilogue.
 //   * main kernel family by M: skinny (M <= 16 rows, K split over the four
@@ -38,31 +40,48 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   p.layout_id = SPEAR_LAYOUT_ID;
   p.M = d.M; p.K = d.K; p.N = d.N; p.rank = d.rank;
   p.cus = cus;
+  const bool skinny = d.M <= kSkinnyMaxM;
   const bool ec = d.rank > 0 && d.variant != SPEAR_VARIANT_NO_EC;
   if (!ec) {
     p.variant = SPEAR_VARIANT_NO_EC;
-  } else if (d.variant == SPEAR_VARIANT_FUSED) {
-    return SPEAR_ERR_UNSUPPORTED;
+  } else if (d.variant == SPEAR_VARIANT_AUTO) {
+    p.variant = skinny ? SPEAR_VARIANT_FUSED : SPEAR_VARIANT_SPLIT;
   } else {
-    p.variant = SPEAR_VARIANT_SPLIT;
+    p.variant = d.variant;
   }
+  if (p.variant == SPEAR_VARIANT_FUSED && !skinny) return SPEAR_ERR_UNSUPPORTED;
   const int64_t nblk = n_pad(d.N) / 16;
-  if (d.M <= kSkinnyMaxM) {
+  size_t ws = 0;
+  size_t scratch_base = kSyncHeaderBytes;
+  if (p.variant == SPEAR_VARIANT_SPLIT) {
+    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank);
+    if (L.m_tiles > kMaxSyncWords) return SPEAR_ERR_UNSUPPORTED;
+    ws = L.bytes;
+    scratch_base = L.bytes;
+    p.ec_split = L.splits;
+    p.producers = L.m_tiles * L.splits;
+  }
+  if (skinny) {
+    const SkinnyShape sh = skinny_shape(d.M, d.K, d.N, d.rank, p.variant == SPEAR_VARIANT_FUSED, cus,
+                                        scratch_base);
+    if (!sh.sync_ok) return SPEAR_ERR_UNSUPPORTED;
     p.kernel = 0;
-    p.tile_m = 16; p.tile_n = 16;
-    p.grid = (int32_t)(nblk * ceil_div(d.M, 16));
+    p.tile_m = 16;
+    p.tile_n = sh.nbw * 16;
+    p.split_k = sh.S;
+    p.grid = sh.P + sh.T * sh.S;
+    if (p.variant == SPEAR_VARIANT_FUSED) {
+      p.producers = sh.P;
+      p.ec_split = sh.P;
+    }
+    if (sh.ws_bytes > ws) ws = sh.ws_bytes;
   } else {
     p.kernel = 1;
     p.tile_m = 128; p.tile_n = 128;
+    p.split_k = 1;
     p.grid = (int32_t)(ceil_div(nblk, 8) * ceil_div(d.M, 128));
   }
-  p.split_k = 1;
-  if (p.variant == SPEAR_VARIANT_SPLIT) {
-    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank);
-    p.producers = L.m_tiles * L.splits;
-    p.ec_split = L.splits;
-    p.workspace_bytes = L.bytes;
-  }
+  p.workspace_bytes = d.M > 0 ? ws : 0;
   *plan = p;
   return SPEAR_OK;
 }
