@@ -126,7 +126,9 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
  * Host only; touches the device only to read its CU count when
  * desc->device_cus == 0 (cached per device).
  * Rules: rank 0 or variant NO_EC -> NO_EC; AUTO -> FUSED when M is at most
- * the skinny-kernel limit (16 rows), else SPLIT.  The per-token gate-value
+ * the skinny-kernel limit (16 rows), else SPLIT.  FUSED with more than 16
+ * rows, and the tiled kernel (M > 16) with X or the packed weight above
+ * 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value
  * decision (skip the EC term of a tile whose gates are all below tau) is
  * taken on the device inside the epilogue, so no gate value ever crosses to
  * the host.

@@ -81,6 +81,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ half8_t buffer_load_half8(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset) {
   return __builtin_bit_cast(half8_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
+// 16-byte device-coherent load (cache policy sc1, as a device-scope atomic
+// load uses), for data other workgroups published with device-coherent stores.
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ float4_t buffer_load_f4_dev(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset) {
+  return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kCachePolicySc1));
+}
 
 // ---------------------------------------------------------------------------
 // Cross-workgroup exchange without L2 write-backs.  Workgroups on different

@@ -1,5 +1,5 @@
-// W4 GEMM with the gated EC term in its epilogue (SPEAR abstract: "fuse the
-// post-EC computation into low-bit GEMMs"):
+// Tiled (prefill, M > 16) W4 GEMM with the gated EC term in its epilogue
+// (SPEAR abstract: "fuse the post-EC computation into low-bit GEMMs"):
 //
 //   acc[m, n] = sum_k X[m, k] q[k, n]                  (fp16 x fp16 -> fp32 MFMA)
 //   Y[m, n]   = fp16( s[n] acc[m, n] + sum_j (g'[m] P[m, j]) B[j, n] )
@@ -10,6 +10,17 @@
 // term two orders of magnitude below Y) and multiplied by B with fp32
 // accumulation.  A wave whose rows all have g' = 0 skips the EC term (the
 // device-side gate-value decision of the dispatcher).
+//
+// Data flow per 128-k step (one packed chunk per 16-column panel):
+//   * X tile [TM x 128] fp16 -> LDS by direct 16-byte copies (no VGPRs), two
+//     stages; units of 16 bytes are XOR-swizzled by row so the fragment reads
+//     of 16 rows hit 16 different bank groups;
+//   * packed int4 weights -> VGPRs, one step ahead (16 bytes per lane = the B
+//     operand of four 32-k blocks);
+//   * one barrier per step: after it, stage s is complete and every wave is
+//     done with stage s-1, whose buffer the copies for step s+1 then refill.
+// Tiles are ordered so that the workgroups of one row of tiles run on one XCD
+// (blocks are dealt round-robin to the 8 XCDs), keeping that X row in one L2.
 #include "device_common.h"
 #include "internal.h"
 
@@ -18,6 +29,10 @@ namespace spear {
 namespace {
 
 constexpr int kGemmThreads = 256;
+constexpr int kKt = 128;                 // k per step (one packed chunk)
+constexpr int kUnitsPerRow = kKt / 8;    // 16-byte units per X row per step
+constexpr int kEcChunk = 64;             // rank columns per epilogue pass
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct GemmKArgs {
   const half_t* X;
@@ -28,138 +43,221 @@ struct GemmKArgs {
   const float* g;
   half_t* Y;
   int M, K, N, rank, KC, NBLK, ps, ec;
+  int MT, NT;             // row and column tiles
 };
 
-// Wave tile MB x NB blocks of 16 x 16; workgroup WM x WN wave tiles; WK waves
-// share the K range of one tile and add their sums through LDS.
-template <int MB, int NB, int WM, int WN, int WK>
-__global__ void __launch_bounds__(kGemmThreads) w4_gemm_kernel(GemmKArgs a) {
-  static_assert(WM * WN * WK * kWave == kGemmThreads, "four waves");
-  constexpr int TM = 16 * MB * WM;
-  constexpr int NBW = NB * WN;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int c16 = lane % 16, t = lane / 16;
-  const int wm = wave % WM, wn = (wave / WM) % WN, wk = wave / (WM * WN);
-  const int row0 = blockIdx.y * TM + wm * MB * 16;
-  const int nb0 = blockIdx.x * NBW + wn * NB;
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void copy2_to_lds(const void* src, void* dst_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 2, 0, 0);
+}
 
-  float4_t acc[MB][NB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = zero_float4();
+// Wave tile MBW x NBW blocks of 16 x 16; workgroup WM x WN waves.
+template <int MBW, int NBW, int WM, int WN>
+__global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a) {
+  static_assert(WM * WN * kWave == kGemmThreads, "four waves");
+  constexpr int TM = 16 * MBW * WM;
+  constexpr int TN = 16 * NBW * WN;
+  constexpr int kStageHalves = TM * kKt;                    // one X stage
+  constexpr int kCopiesPerWave = TM * kUnitsPerRow / kWave / 4;
+  static_assert(kEcChunk * TN * 4 + TM * kEcChunk * 2 <= 2 * TM * kKt * 2, "EC chunk fits the X stages");
+  extern __shared__ __align__(16) unsigned char lds[];
+  half_t* xs = reinterpret_cast<half_t*>(lds);                // [2][TM][kKt], swizzled units
 
-  for (int kc = wk; kc < a.KC; kc += WK) {
-    u32x4_t bw[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int gnb = nb0 + nb;
-      if (gnb < a.NBLK) {
-        bw[nb] = a.Wq[((size_t)gnb * a.KC + kc) * kWave + lane];
-      } else {
-        bw[nb] = (u32x4_t){kZeroCodeWord, kZeroCodeWord, kZeroCodeWord, kZeroCodeWord};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kx = kc * kKChunk + j * 32 + t * 8;
-      half8_t xa[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = row0 + mb * 16 + c16;
-        xa[mb] = (row < a.M && kx < a.K) ? load_half8(a.X + (size_t)row * a.K + kx) : zero_half8();
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const half8_t b = decode_w4(bw[nb][j]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = mfma16x16x32(xa[mb], b, acc[mb][nb]);
-      }
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int c16 = lane % 16, t4 = lane / 16;
+  const int wm = w % WM, wn = w / WM;
+
+  // Tile order: with a multiple of 8 row tiles, XCD x (block % 8) takes row
+  // tiles x, x + 8, ... and walks the column tiles of each.
+  int m_tile, n_tile;
+  {
+    const int bid = blockIdx.x;
+    if (a.MT % 8 == 0) {
+      const int xcd = bid % 8, j = bid / 8;
+      m_tile = xcd + 8 * (j / a.NT);
+      n_tile = j % a.NT;
+    } else {
+      m_tile = bid / a.NT;
+      n_tile = bid % a.NT;
     }
   }
+  const int m0 = m_tile * TM, nb_base = n_tile * (NBW * WN) + wn * NBW;
 
-  if constexpr (WK > 1) {
-    __shared__ float4_t red[WK - 1][WM * WN][kWave][MB * NB];
-    const int slot = wm + WM * wn;
-    if (wk > 0) {
+  // ---- X tile copies for step kc into stage st, through a buffer resource
+  // over X: rows >= M fall outside it and units at k >= K are sent outside
+  // it, so both read as zeros.  Copy i of wave w fills rows (w * kCopiesPerWave + i) * 4
+  // .. + 3; lane L writes slot L % 16 of row L / 16, holding the source unit
+  // (slot ^ (row % 16)).
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
+  const uint32_t row_bytes = (uint32_t)a.K * 2u;
+  auto issue_x = [&](int kc, int st) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) red[wk - 1][slot][lane][mb * NB + nb] = acc[mb][nb];
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      const int row = (w * kCopiesPerWave + i) * 4 + lane / 16;
+      const int unit = (lane % 16) ^ (row % 16);
+      const int k = kc * kKt + unit * 8;
+      const uint32_t voff = k < a.K ? (uint32_t)(m0 + row) * row_bytes + (uint32_t)k * 2u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (lds_void_t*)(xs + (size_t)st * kStageHalves + (size_t)(row - lane / 16) * kKt), 16, voff, 0, 0, 0);
     }
+  };
+  // Packed weights through a buffer resource (panels >= NBLK clamped: their
+  // columns are never stored).
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.Wq, (uint32_t)((size_t)a.NBLK * a.KC * 1024));
+  auto load_w = [&](int kc, u32x4_t* dst) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const uint32_t voff = ((uint32_t)min(nb_base + nb, a.NBLK - 1) * (uint32_t)a.KC * 64u + (uint32_t)lane) * 16u;
+      dst[nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, kc * 1024, 0));
+    }
+  };
+
+  float4_t acc[MBW][NBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[i][j] = zero_float4();
+
+  u32x4_t wcur[NBW], wnext[NBW];
+  issue_x(0, 0);
+  load_w(0, wcur);
+  for (int kc = 0; kc < a.KC; ++kc) {
+    const int st = kc & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (wk > 0) return;
+    if (kc + 1 < a.KC) {
+      issue_x(kc + 1, st ^ 1);
+      load_w(kc + 1, wnext);
+    }
+    const half_t* xst = xs + (size_t)st * kStageHalves;
 #pragma unroll
-    for (int w = 0; w < WK - 1; ++w)
+    for (int j = 0; j < 4; ++j) {
+      half8_t af[MBW];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MBW; ++mb) {
+        const int row = wm * MBW * 16 + mb * 16 + c16;
+        const int slot = (j * 4 + t4) ^ (row % 16);
+        af[mb] = *reinterpret_cast<const half8_t*>(xst + (size_t)row * kKt + slot * 8);
+      }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] += red[w][slot][lane][mb * NB + nb];
+      for (int nb = 0; nb < NBW; ++nb) {
+        const half8_t bf = decode_w4(wcur[nb][j]);
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = mfma16x16x32(af[mb], bf, acc[mb][nb]);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) wcur[nb] = wnext[nb];
   }
 
   // ---------------------------------------------------------------- epilogue
-  const int jblocks = a.ps / 32;
-  bool any_gate = false;
-  if (a.ec) {
+  // acc <- s acc, then the EC term accumulates onto it on the matrix cores,
+  // 64 rank columns at a time.  For each chunk the LDS (free once every wave
+  // is done with the X stages) holds the B rows bs[64][TN] (dword slots, fp16
+  // in the low half; rows >= rank clamped: they meet zero P columns) and
+  // pg[TM][64] = fp16(g' P) of the tile's rows (rows >= M clamped: never
+  // stored).
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = row0 + mb * 16 + c16;
-      any_gate |= (row < a.M) && (a.g[row] != 0.0f);
-    }
+  for (int nb = 0; nb < NBW; ++nb) {
+    const float s = (float)a.scales[min((nb_base + nb) * 16 + c16, a.N - 1)];
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] *= s;
+  }
+  const int jblocks = a.ec ? a.ps / 32 : 0;
+  bool any_gate = false;
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int row = m0 + wm * MBW * 16 + mb * 16 + c16;
+    any_gate |= jblocks > 0 && row < a.M && a.g[min(row, a.M - 1)] != 0.0f;
   }
   any_gate = __any(any_gate);
-
+  uint32_t* bs = reinterpret_cast<uint32_t*>(lds);
+  half_t* pg = reinterpret_cast<half_t*>(lds + (size_t)kEcChunk * TN * 4);
+  const int n0 = n_tile * TN;
+  for (int j0 = 0; j0 < jblocks * 32; j0 += kEcChunk) {
+    __syncthreads();
+    for (int e = w * kWave; e < kEcChunk * TN; e += 4 * kWave) {
+      const int idx = e + lane, r = idx / TN, c = idx % TN;
+      copy2_to_lds(a.B + (size_t)min(j0 + r, a.rank - 1) * a.N + min(n0 + c, a.N - 1), bs + e);
+    }
+    for (int idx = tid; idx < TM * (kEcChunk / 4); idx += kGemmThreads) {
+      const int r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
+      const int row = min(m0 + r, a.M - 1);
+      const int col = j0 + c4 * 4;
+      const float gv = a.g[row];
+      float4_t pv = zero_float4();
+      if (col < a.ps) pv = *reinterpret_cast<const float4_t*>(a.P + (size_t)row * a.ps + col);
+      half_t* dst = pg + (size_t)r * kEcChunk + c4 * 4;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = (nb0 + nb) * 16 + c16;
-    const float s = col < a.N ? (float)a.scales[col] : 0.0f;
-    float4_t ecacc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) ecacc[mb] = zero_float4();
+      for (int e = 0; e < 4; ++e) dst[e] = (half_t)(gv * pv[e]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     if (any_gate) {
-      for (int jb = 0; jb < jblocks; ++jb) {
-        half8_t bb;
+      const int jbn = min(kEcChunk, jblocks * 32 - j0) / 32;
+      for (int jb = 0; jb < jbn; ++jb) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = jb * 32 + t * 8 + e;
-          bb[e] = (j < a.rank && col < a.N) ? a.B[(size_t)j * a.N + col] : (half_t)0.0f;
-        }
+        for (int nb = 0; nb < NBW; ++nb) {
+          const int lc = (wn * NBW + nb) * 16 + c16;
+          half8_t bb;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int row = row0 + mb * 16 + c16;
-          half8_t pa = zero_half8();
-          if (row < a.M) {
-            const float gv = a.g[row];
-            const float* pr = a.P + (size_t)row * a.ps + jb * 32 + t * 8;
+          for (int e = 0; e < 8; ++e)
+            bb[e] = __builtin_bit_cast(half_t, (uint16_t)bs[(jb * 32 + t4 * 8 + e) * TN + lc]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pa[e] = (half_t)(gv * pr[e]);
+          for (int mb = 0; mb < MBW; ++mb) {
+            const int r = wm * MBW * 16 + mb * 16 + c16;
+            const half8_t pa = *reinterpret_cast<const half8_t*>(pg + (size_t)r * kEcChunk + jb * 32 + t4 * 8);
+            acc[mb][nb] = mfma16x16x32(pa, bb, acc[mb][nb]);
           }
-          ecacc[mb] = mfma16x16x32(pa, bb, ecacc[mb]);
         }
       }
     }
-    if (col < a.N) {
+  }
+
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int col = (nb_base + nb) * 16 + c16;
+    if (col >= a.N) continue;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = row0 + mb * 16 + 4 * t + v;
-          if (row < a.M) a.Y[(size_t)row * a.N + col] = (half_t)fmaf(s, acc[mb][nb][v], ecacc[mb][v]);
-        }
+    for (int mb = 0; mb < MBW; ++mb) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm * MBW * 16 + mb * 16 + 4 * t4 + v;
+        if (row < a.M) a.Y[(size_t)row * a.N + col] = (half_t)acc[mb][nb][v];
+      }
     }
   }
 }
 
-template <int MB, int NB, int WM, int WN, int WK>
-hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
-  constexpr int TM = 16 * MB * WM, NBW = NB * WN;
-  const dim3 grid((unsigned)ceil_div(k.NBLK, NBW), (unsigned)ceil_div(k.M, TM));
-  hipLaunchKernelGGL((w4_gemm_kernel<MB, NB, WM, WN, WK>), grid, dim3(kGemmThreads), 0,
-                     (hipStream_t)stream, k);
+template <int MBW, int NBW, int WM, int WN>
+hipError_t launch_cfg(GemmKArgs k, void* stream) {
+  constexpr int TM = 16 * MBW * WM, TNB = NBW * WN;
+  k.MT = (int)ceil_div(k.M, TM);
+  k.NT = (int)ceil_div(k.NBLK, TNB);
+  const size_t lds = (size_t)2 * TM * kKt * 2;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN>), dim3((unsigned)(k.MT * k.NT)),
+                     dim3(kGemmThreads), lds, (hipStream_t)stream, k);
   return hipGetLastError();
 }
 
 }  // namespace
+
+TiledShape tiled_shape(int64_t M, int64_t N) {
+  // 256-row tiles; 224 columns when that gives whole waves of 256 tiles.
+  TiledShape t;
+  const int64_t nblk = n_pad(N) / 16;
+  t.tm = 256;
+  t.tn = (nblk % 14 == 0 && nblk >= 14) ? 224 : 256;
+  t.grid = (int)(ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16));
+  return t;
+}
 
 hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream) {
   GemmKArgs k;
@@ -175,8 +273,9 @@ hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream
   k.NBLK = (int)(n_pad(a.N) / kNBlock);
   k.ps = a.ec ? (int)p_stride(a.rank) : 0;
   k.ec = a.ec;
-  if (plan.kernel == 0) return launch_cfg<1, 1, 1, 1, 4>(k, stream);
-  return launch_cfg<4, 4, 2, 2, 1>(k, stream);
+  k.MT = k.NT = 0;
+  if (plan.tile_n == 224) return launch_cfg<8, 7, 2, 2>(k, stream);
+  return launch_cfg<8, 8, 2, 2>(k, stream);
 }
 
 }  // namespace spear

@@ -93,7 +93,7 @@ struct SkinnyShape {
   int ksp = 0;      // k per producer slab
   size_t lds = 0;   // dynamic LDS of a producer
   size_t lds_gemm = 0;  // dynamic LDS of a GEMM workgroup (EC factor tile)
-  size_t ws_sync = 0, ws_ec_part = 0, ws_ec_final = 0, ws_gemm_part = 0;
+  size_t ws_sync = 0, ws_ec_part = 0, ws_gemm_part = 0;
   size_t ws_bytes = 0;   // total workspace (0: none needed)
   bool sync_ok = true;   // the tile counters fit the counter header
 };
@@ -118,6 +118,12 @@ struct SkinnyLaunch {
   const float* gext;
 };
 hipError_t launch_skinny(const SkinnyLaunch& L, void* stream);
+
+// Tiled (M > 16) kernel: tile shape and grid.
+struct TiledShape {
+  int tm = 256, tn = 256, grid = 0;
+};
+TiledShape tiled_shape(int64_t M, int64_t N);
 
 hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);

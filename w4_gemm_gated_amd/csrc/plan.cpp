@@ -10,8 +10,7 @@
 //     launch, then the tiled GEMM with the gated epilogue);
 //   * the per-token gate-value decision (skip the EC term where every gate of
 //     a wave's rows is below tau) is taken on the device in the epilogue.
-//   * main kernel family by M: skinny (M <= 16 rows, K split over the four
-//     waves of a workgroup) or tiled (128 x 128 tiles).
+//   * main kernel family by M: skinny (M <= 16 rows) or tiled (256-row tiles).
 #include <cmath>
 #include <cstring>
 
@@ -50,7 +49,6 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     p.variant = d.variant;
   }
   if (p.variant == SPEAR_VARIANT_FUSED && !skinny) return SPEAR_ERR_UNSUPPORTED;
-  const int64_t nblk = n_pad(d.N) / 16;
   size_t ws = 0;
   size_t scratch_base = kSyncHeaderBytes;
   if (p.variant == SPEAR_VARIANT_SPLIT) {
@@ -76,10 +74,14 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     }
     if (sh.ws_bytes > ws) ws = sh.ws_bytes;
   } else {
+    // X and the packed weight are addressed with 32-bit buffer offsets.
+    if ((int64_t)d.M * d.K * 2 > INT32_MAX || n_pad(d.N) * k_pad(d.K) / 2 > INT32_MAX)
+      return SPEAR_ERR_UNSUPPORTED;
+    const TiledShape t = tiled_shape(d.M, d.N);
     p.kernel = 1;
-    p.tile_m = 128; p.tile_n = 128;
+    p.tile_m = t.tm; p.tile_n = t.tn;
     p.split_k = 1;
-    p.grid = (int32_t)(ceil_div(nblk, 8) * ceil_div(d.M, 128));
+    p.grid = t.grid;
   }
   p.workspace_bytes = d.M > 0 ? ws : 0;
   *plan = p;

@@ -16,7 +16,8 @@
 //   * the P producers (lowest block indices: dispatched first, never waiting)
 //     each compute [P | z] = X [A | w_g] over one K slab and publish it; every
 //     tile finisher waits (bounded) until all P slabs are published, adds them
-//     in fixed order, applies the gate and runs the EC epilogue.
+//     in fixed order (16-byte device-coherent loads), applies the gate and
+//     runs the EC epilogue.
 // Data crosses workgroups only through device-coherent stores and loads (see
 // device_common.h), never through L2 write-backs.  Every call returns its
 // counters to zero.
@@ -30,6 +31,10 @@ namespace {
 constexpr int kThreads = 256;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Sync words, each hot one on its own 128-byte line (pollers and updaters of
+// different words then never contend for one line).
+constexpr int kSlabs = 0, kFinishers = 32, kError = 64, kTiles = 96;
+
 struct SkinnyKArgs {
   const half_t* X;
   const u32x4_t* Wq;
@@ -42,9 +47,9 @@ struct SkinnyKArgs {
   int T, S, CPS, P, ksp, R1p, ps;
   int ec_mode;            // 0: no EC; 1: fused producers; 2: P and g given (split variant)
   float gate_bias, skip_tau;
-  uint32_t* sync;         // [0] producers done, [1] finishers done, [2] error, [3] ready, [4+t] tiles
-  float* ec_part;         // [P][16][rank + 1]
-  float* ec_final;        // [16][rank + 1]
+  uint32_t* sync;         // [kSlabs] slabs published, [kFinishers] finishers past the wait,
+                          // [kError] error, [kTiles + t] split-K tile counters
+  float* ec_part;         // [P][16][r1p4], r1p4 = rank + 1 rounded up to 4
   float* gemm_part;       // [T*S][NBW][64][4]
   const float* Pext;      // ec_mode 2: [M][ps]
   const float* gext;      // ec_mode 2: [M]
@@ -136,8 +141,10 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
   // Column blocks in passes of kPass: blocks 0 .. pblocks-1 hold P (columns
   // >= rank clamped, never published); in the first pass, an extra block
   // holds the gate logit in its column 0.  Each wave sums its k-blocks, then
-  // the four waves add up through LDS and publish rows 4 t4 .. 4 t4 + 3.
-  float* part = a.ec_part + (size_t)p * 16 * r1;
+  // the four waves add up through LDS and publish rows 4 t4 .. 4 t4 + 3 of
+  // this slab's [P | z] (row stride r1p4 = rank + 1 rounded up to 4).
+  const int r1p4 = (r1 + 3) & ~3;
+  float* part = a.ec_part + (size_t)p * 16 * r1p4;
   for (int nb0 = 0; nb0 < pblocks; nb0 += kPass) {
     float4_t acc[kPass + 1];
 #pragma unroll
@@ -176,43 +183,14 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
       const int col = gate ? a.rank : (nb0 + j) * 16 + c16;
       if (gate ? c16 == 0 : col < a.rank) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) st_dev(&part[(4 * t4 + v) * r1 + col], sum[v]);
+        for (int v = 0; v < 4; ++v) st_dev(&part[(4 * t4 + v) * r1p4 + col], sum[v]);
       }
     }
   }
+  // Publish: drain the stores, then count this slab in.
   drain_vm();
   __syncthreads();
-  __shared__ uint32_t last;
-  if (tid == 0) last = (add_dev_u32(&a.sync[0], 1u) == (uint32_t)(a.P - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!last) return;
-
-  // Last producer: fixed-order sum of the slabs -> final [P | z] (16 x (rank + 1)),
-  // then raise the ready flag.  Loads use clamped indices and a select, a
-  // thread's loads all in flight together.
-  const size_t stride = (size_t)16 * r1;
-  const int n = 16 * r1;
-  for (int base = 0; base < n; base += 4 * kThreads) {
-    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p0 = 0; p0 < a.P; p0 += 8) {
-      float part8[4][8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          part8[u][q] = ld_dev(a.ec_part + (size_t)min(p0 + q, a.P - 1) * stride + min(base + u * kThreads + tid, n - 1));
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[u] += p0 + q < a.P ? part8[u][q] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (base + u * kThreads + tid < n) st_dev(&a.ec_final[base + u * kThreads + tid], v[u]);
-  }
-  drain_vm();
-  __syncthreads();
-  if (tid == 0) st_dev_u32(&a.sync[3], 1u);
+  if (tid == 0) add_dev_u32(&a.sync[kSlabs], 1u);
 }
 
 // ---------------------------------------------------------------- GEMM tile
@@ -329,7 +307,7 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) st_dev(&slot[(nb * kWave + lane) * 4 + v], acc[nb][v]);
       drain_vm();
-      if (lane == 0) last_s = (add_dev_u32(&a.sync[4 + t], 1u) == (uint32_t)(a.S - 1)) ? 1u : 0u;
+      if (lane == 0) last_s = (add_dev_u32(&a.sync[kTiles + t], 1u) == (uint32_t)(a.S - 1)) ? 1u : 0u;
     }
     __syncthreads();
     if (!last_s) return;
@@ -343,28 +321,42 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[nb][v] += ld_dev(&sl[(nb * kWave + lane) * 4 + v]);
       }
-      if (lane == 0) st_dev_u32(&a.sync[4 + t], 0u);
+      if (lane == 0) st_dev_u32(&a.sync[kTiles + t], 0u);
     }
   }
 
-  // ---- EC projection of the 16 rows -> Pc (all four waves)
+  // ---- EC projection of the 16 rows -> Pc (all four waves): wait until the
+  // P slabs are published, then add them in fixed order.  The finisher count
+  // is bumped right after the wait; its result (last finisher resets the
+  // counters) is needed only at the very end.
+  uint32_t finishers_before = 0;
   if (a.ec_mode == 1) {
     if (tid == 0) {
       uint32_t n = 0;
-      while (ld_dev_u32(&a.sync[3]) == 0u) {
-        if (++n > a.spin_limit) { st_dev_u32(&a.sync[2], 1u); break; }
-        __builtin_amdgcn_s_sleep(2);
+      while (ld_dev_u32(&a.sync[kSlabs]) < (uint32_t)a.P) {
+        if (++n > a.spin_limit) { st_dev_u32(&a.sync[kError], 1u); break; }
+        __builtin_amdgcn_s_sleep(8);
       }
+      finishers_before = add_dev_u32(&a.sync[kFinishers], 1u);
     }
     __syncthreads();
-    {
-      const int n = 16 * r1;                       // <= 16 * 257: at most 17 per thread
-      float v[17];
+    const int r1p4 = (r1 + 3) & ~3, u4 = r1p4 / 4;
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.ec_part, (uint32_t)((size_t)a.P * 16 * r1p4 * 4));
+    for (int unit = tid; unit < 16 * u4; unit += kThreads) {
+      float4_t sum = zero_float4();
+      for (int p0 = 0; p0 < a.P; p0 += 8) {
+        float4_t v[8];
 #pragma unroll
-      for (int u = 0; u < 17; ++u) v[u] = ld_dev(&a.ec_final[min(u * kThreads + tid, n - 1)]);
+        for (int q = 0; q < 8; ++q)
+          v[q] = buffer_load_f4_dev(pr, (uint32_t)((min(p0 + q, a.P - 1) * 16 * u4 + unit) * 16));
 #pragma unroll
-      for (int u = 0; u < 17; ++u)
-        if (u * kThreads + tid < n) Pc[u * kThreads + tid] = v[u];
+        for (int q = 0; q < 8; ++q)
+          if (p0 + q < a.P) sum += v[q];
+      }
+      const int row = unit / u4, c0 = (unit % u4) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c0 + e < r1) Pc[row * r1 + c0 + e] = sum[e];
     }
     __syncthreads();
   } else if (a.ec_mode == 2) {
@@ -423,13 +415,11 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
     }
   }
 
-  // The last finisher resets the producer counter and the flag for the next call.
-  if (a.ec_mode == 1 && lane == 0) {
-    if (add_dev_u32(&a.sync[1], 1u) == (uint32_t)(a.T - 1)) {
-      st_dev_u32(&a.sync[0], 0u);
-      st_dev_u32(&a.sync[3], 0u);
-      st_dev_u32(&a.sync[1], 0u);
-    }
+  // The last finisher past the wait resets the counters for the next call
+  // (every finisher has seen all slabs by then).
+  if (a.ec_mode == 1 && lane == 0 && finishers_before == (uint32_t)(a.T - 1)) {
+    st_dev_u32(&a.sync[kSlabs], 0u);
+    st_dev_u32(&a.sync[kFinishers], 0u);
   }
 }
 
@@ -514,13 +504,10 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
   size_t off = scratch_base;
   auto take = [&](size_t bytes) { size_t o = off; off = (size_t)round_up((int64_t)(off + bytes), 256); return o; };
   sh.ws_sync = kGemmSyncOffset;
-  if (sh.P > 0) {
-    sh.ws_ec_part = take(sizeof(float) * (size_t)sh.P * 16 * (size_t)(rank + 1));
-    sh.ws_ec_final = take(sizeof(float) * 16 * (size_t)(rank + 1));
-  }
+  if (sh.P > 0) sh.ws_ec_part = take(sizeof(float) * (size_t)sh.P * 16 * (size_t)round_up(rank + 1, 4));
   if (sh.S > 1) sh.ws_gemm_part = take(sizeof(float) * 4 * kWave * (size_t)sh.nbw * sh.T * sh.S);
   sh.ws_bytes = (sh.S > 1 || sh.P > 0) ? off : 0;
-  sh.sync_ok = 4 + sh.T <= kMaxSyncWords;
+  sh.sync_ok = kTiles + sh.T <= kMaxSyncWords;
   (void)M;
   return sh;
 }
@@ -548,11 +535,10 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream) {
   char* ws = (char*)L.workspace;
   k.sync = (uint32_t*)(ws + sh.ws_sync);   // absolute offsets from the workspace base
   k.ec_part = (float*)(ws + sh.ws_ec_part);
-  k.ec_final = (float*)(ws + sh.ws_ec_final);
   k.gemm_part = (float*)(ws + sh.ws_gemm_part);
   k.Pext = L.Pext;
   k.gext = L.gext;
-  k.spin_limit = 1u << 22;
+  k.spin_limit = 1u << 20;   // ~0.5 s of polling: far beyond any healthy wait
   size_t lds = k.P > 0 ? sh.lds : 0;
   if (L.ec_mode && sh.lds_gemm > lds) lds = sh.lds_gemm;
   const bool exact = sh.CPS == 4 * sh.CPW && (int64_t)sh.CPS * sh.S == k.KC;
