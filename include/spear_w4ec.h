@@ -126,9 +126,9 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
  * Host only; touches the device only to read its CU count when
  * desc->device_cus == 0 (cached per device).
  * Rules: rank 0 or variant NO_EC -> NO_EC; AUTO -> FUSED when M is at most
- * the skinny-kernel limit (16 rows), else SPLIT.  FUSED with more than 16
- * rows, and the tiled kernel (M > 16) with X or the packed weight above
- * 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value
+ * the skinny-kernel limit (16 rows) and rank % 4 == 0, else SPLIT.  FUSED
+ * outside those limits, and the tiled kernel (M > 16) with X or the packed
+ * weight above 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value
  * decision (skip the EC term of a tile whose gates are all below tau) is
  * taken on the device inside the epilogue, so no gate value ever crosses to
  * the host.
@@ -150,11 +150,15 @@ spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t
  *            accumulation; must not alias any input.
  *   workspace  device memory of at least plan.workspace_bytes (16-byte
  *            aligned; may be NULL when that is 0).  It must be zero-filled
- *            before its first use.  Its first 64 KiB hold cross-workgroup
- *            counters, which every call returns to zero; the rest is
- *            scratch.  So a zero-filled workspace can be reused, without
- *            clearing, by later calls of any plan that fit in it.  Calls
- *            that run concurrently must not share a workspace.
+ *            before its first use.  Its first 256 KiB are a header owned by
+ *            the library: cross-workgroup counters, which every call returns
+ *            to zero, a call epoch, which every fused call advances by one,
+ *            and the fused variant's hand-off slabs, whose entries carry the
+ *            epoch of the call that wrote them.  The rest is scratch.  So a
+ *            zero-filled workspace can be reused, without clearing, by later
+ *            calls of any plan that fit in it; the caller must not write to
+ *            it between calls.  Calls that run concurrently must not share a
+ *            workspace.
  * Errors: NULL_POINTER, INVALID_SHAPE, INVALID_ARGUMENT, MISALIGNED,
  *         WORKSPACE_TOO_SMALL, INVALID_PLAN, UNSUPPORTED, HIP.
  */

@@ -70,7 +70,15 @@ def test_dispatch_rules(lib):
     st, p = plan(lib, 2048, 4096, 14336, 64)
     assert st == 0 and p.variant == 2 and p.kernel == 1 and p.workspace_bytes > 0
     st, p = plan(lib, 16, 4096, 4096, 32)
-    assert p.variant == 1 and p.producers > 0 and p.grid > p.producers
+    # fused: the EC producer workgroups, then the GEMM tiles (256 panels of
+    # 16 columns, one K range)
+    assert p.variant == 1 and p.producers == 8 and p.grid == 256 + 8 and p.split_k == 1
+    st, p = plan(lib, 4, 4096, 4096, 30)
+    assert st == 0 and p.variant == 2     # fused needs rank % 4 == 0: auto takes split
+    st, p = plan(lib, 4, 4096, 4096, 30, variant=1)
+    assert st == 3
+    st, p = plan(lib, 40000, 60000, 4096, 16)
+    assert st == 3                        # X above 2^31 - 1 bytes for the tiled kernel
     st, p = plan(lib, 16, 4096, 4096, 0)
     assert st == 0 and p.variant == 3 and p.producers == 0
     st, p = plan(lib, 16, 4096, 4096, 32, variant=2)

@@ -175,6 +175,15 @@ def test_ragged_shapes(M, K, N, r):
     layer_case(X, W, A, B, w_g, 0.25, 0.0, "auto", f"ragged M={M} K={K} N={N} r={r}")
 
 
+@pytest.mark.parametrize("M,K,N,r", [(3, 136, 20, 4), (16, 1000, 100, 20), (7, 264, 40, 36), (4, 512, 48, 256),
+                                     (1, 8, 1, 4), (16, 2056, 4096, 32)])
+def test_fused_ragged_shapes(M, K, N, r):
+    """The single-launch variant on K tails (K % 32 != 0), partial column
+    blocks of A (rank % 16 != 0), one-column outputs and the largest rank."""
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=3 * M + K + N + r, outliers=True)
+    layer_case(X, W, A, B, w_g, -0.5, 0.0, "fused", f"fused ragged M={M} K={K} N={N} r={r}")
+
+
 def test_empty_batch():
     w = workloads.workload(1)
     Wq_d, s_d = sp.spear_pack_w4(cuda(w["W"]))
@@ -214,8 +223,13 @@ def test_repeat_calls_deterministic_and_workspace_clean():
     Y2 = sp.spear_w4ec_linear(*args, plan=p, workspace=ws).clone()
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
-    # the 64 KiB counter header is back at zero; the rest is scratch
-    assert int(ws[: 64 * 1024].view(torch.int32).abs().sum().item()) == 0
+    # the counters of the header are back at zero, and the call epoch (word 96
+    # of the GEMM counter region at 32 KiB) counts the two fused calls
+    counters = ws[: 64 * 1024].view(torch.int32).clone()
+    epoch_word = 32 * 1024 // 4 + 96
+    assert int(counters[epoch_word].item()) == 2
+    counters[epoch_word] = 0
+    assert int(counters.abs().sum().item()) == 0
 
 
 @pytest.mark.parametrize("variant", ["fused", "split", "no_ec"])

@@ -68,6 +68,12 @@ __device__ __forceinline__ half8_t load_half8(const half_t* p) {
   return *reinterpret_cast<const half8_t*>(p);
 }
 
+// Bit casts through a by-value parameter.  (This compiler miscompiles
+// __builtin_bit_cast applied directly to a vector element, v[i]: it reads
+// element 0 for every i.  A scalar parameter avoids that form.)
+__device__ __forceinline__ uint32_t float_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bits_float(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // Buffer resource over [base, base + bytes): raw buffer loads at an offset

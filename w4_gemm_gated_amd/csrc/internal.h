@@ -26,14 +26,19 @@ inline int64_t ec_cols(int64_t rank) { return round_up(rank + 1, 16); }
 // Row stride (floats) of the stored P: rank padded to the 32-k granule.
 inline int64_t p_stride(int64_t rank) { return round_up(rank, 32); }
 
-// Every workspace starts with a fixed 64 KiB header of cross-workgroup
-// counters, which every call returns to zero: EC-projection counters in the
-// first half, GEMM counters in the second.  All scratch lies after it, so a
-// zero-filled workspace serves calls of any plan (each plan's counters sit
-// in the header, never in another plan's scratch).
-constexpr size_t kSyncHeaderBytes = 64 * 1024;
+// Every workspace starts with a fixed 256 KiB header: cross-workgroup
+// counters of the EC projection in [0, 32 KiB) and of the GEMM kernels in
+// [32 KiB, 64 KiB), which every call returns to zero (except the GEMM call
+// epoch, which every fused call advances), and the fused variant's hand-off
+// slabs in [64 KiB, 256 KiB), whose entries carry the epoch of the call that
+// wrote them.  All scratch lies after the header, so a zero-filled workspace
+// serves calls of any plan (each plan's counters and hand-off sit in the
+// header, never in another plan's scratch).
+constexpr size_t kSyncHeaderBytes = 256 * 1024;
 constexpr size_t kGemmSyncOffset = 32 * 1024;
-constexpr int64_t kMaxSyncWords = 8192;   // per half of the header
+constexpr size_t kHandoffOffset = 64 * 1024;
+constexpr size_t kHandoffBytes = 192 * 1024;
+constexpr int64_t kMaxSyncWords = 8192;   // per counter region
 
 // Workspace layout of the EC projection (offsets in bytes, 256-aligned).
 struct EcWorkspace {
@@ -55,6 +60,7 @@ spear_status_t check_desc(const spear_linear_desc_t& d);
 
 // Shapes of the main kernel families.
 constexpr int kSkinnyMaxM = 16;   // rows handled by the skinny kernel
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS of one gfx950 workgroup
 
 // ----------------------------------------------------------------- launchers
 
@@ -93,9 +99,9 @@ struct SkinnyShape {
   int ksp = 0;      // k per producer slab
   size_t lds = 0;   // dynamic LDS of a producer
   size_t lds_gemm = 0;  // dynamic LDS of a GEMM workgroup (EC factor tile)
-  size_t ws_sync = 0, ws_ec_part = 0, ws_gemm_part = 0;
+  size_t ws_sync = 0, ws_handoff = 0, ws_gemm_part = 0;
   size_t ws_bytes = 0;   // total workspace (0: none needed)
-  bool sync_ok = true;   // the tile counters fit the counter header
+  bool fits = true;      // counters and hand-off fit the header, LDS fits
 };
 // scratch_base: first byte of the workspace this kernel may use as scratch.
 SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fused, int cus,

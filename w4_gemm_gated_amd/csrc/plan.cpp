@@ -4,9 +4,9 @@
 //
 // Decisions:
 //   * no EC (rank 0) or variant NO_EC            -> NO_EC: the W4 GEMM alone;
-//   * AUTO, M <= 16 rows                         -> FUSED: one launch (EC
+//   * AUTO, M <= 16 rows and rank % 4 == 0       -> FUSED: one launch (EC
 //     producers, split-K W4 GEMM, gated epilogue);
-//   * AUTO, M > 16                               -> SPLIT (EC projection
+//   * AUTO otherwise (M > 16, or rank % 4 != 0)  -> SPLIT (EC projection
 //     launch, then the tiled GEMM with the gated epilogue);
 //   * the per-token gate-value decision (skip the EC term where every gate of
 //     a wave's rows is below tau) is taken on the device in the epilogue.
@@ -41,14 +41,19 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   p.cus = cus;
   const bool skinny = d.M <= kSkinnyMaxM;
   const bool ec = d.rank > 0 && d.variant != SPEAR_VARIANT_NO_EC;
+  // The fused producers read A with 8-byte transposing LDS reads: rank % 4 == 0.
+  auto fused_ok = [&]() {
+    if (!skinny || d.rank % 4 != 0) return false;
+    return skinny_shape(d.M, d.K, d.N, d.rank, true, cus, kSyncHeaderBytes).fits;
+  };
   if (!ec) {
     p.variant = SPEAR_VARIANT_NO_EC;
   } else if (d.variant == SPEAR_VARIANT_AUTO) {
-    p.variant = skinny ? SPEAR_VARIANT_FUSED : SPEAR_VARIANT_SPLIT;
+    p.variant = fused_ok() ? SPEAR_VARIANT_FUSED : SPEAR_VARIANT_SPLIT;
   } else {
     p.variant = d.variant;
   }
-  if (p.variant == SPEAR_VARIANT_FUSED && !skinny) return SPEAR_ERR_UNSUPPORTED;
+  if (p.variant == SPEAR_VARIANT_FUSED && !fused_ok()) return SPEAR_ERR_UNSUPPORTED;
   size_t ws = 0;
   size_t scratch_base = kSyncHeaderBytes;
   if (p.variant == SPEAR_VARIANT_SPLIT) {
@@ -62,12 +67,12 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   if (skinny) {
     const SkinnyShape sh = skinny_shape(d.M, d.K, d.N, d.rank, p.variant == SPEAR_VARIANT_FUSED, cus,
                                         scratch_base);
-    if (!sh.sync_ok) return SPEAR_ERR_UNSUPPORTED;
+    if (!sh.fits) return SPEAR_ERR_UNSUPPORTED;
     p.kernel = 0;
     p.tile_m = 16;
     p.tile_n = sh.nbw * 16;
     p.split_k = sh.S;
-    p.grid = sh.P + sh.T * sh.S;
+    p.grid = sh.T * sh.S + (p.variant == SPEAR_VARIANT_FUSED ? sh.P : 0);
     if (p.variant == SPEAR_VARIANT_FUSED) {
       p.producers = sh.P;
       p.ec_split = sh.P;

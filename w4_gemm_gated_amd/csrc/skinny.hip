@@ -14,13 +14,22 @@
 //     and the last to arrive (device-scope counter) adds the S partial sums in
 //     fixed order, so results do not depend on timing;
 //   * the P producers (lowest block indices: dispatched first, never waiting)
-//     each compute [P | z] = X [A | w_g] over one K slab and publish it; every
-//     tile finisher waits (bounded) until all P slabs are published, adds them
-//     in fixed order (16-byte device-coherent loads), applies the gate and
-//     runs the EC epilogue.
+//     each compute [P | z] = X [A | w_g] over one K slab for the M rows and
+//     publish it in the hand-off table, each value tagged with the call's
+//     epoch;
+//   * every GEMM workgroup requests the hand-off table right behind its
+//     weight loads.  A CU serves its memory requests in order, so the table
+//     arrives when the workgroup's weight stream has, by which time the
+//     producers (on CUs with no weight stream, and a head start) have
+//     normally published it; the tags tell whether they had, and a bounded
+//     wait covers the entries they had not.  The workgroup adds the slabs in
+//     fixed order and applies the gate itself.
 // Data crosses workgroups only through device-coherent stores and loads (see
 // device_common.h), never through L2 write-backs.  Every call returns its
-// counters to zero.
+// counters to zero and advances the epoch; the last GEMM workgroup to finish
+// does both, when every producer and every reader is done.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -28,12 +37,13 @@ namespace spear {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;          // four waves
+constexpr uint32_t kStreamDelay = 16;  // fused: GEMM head-start delay, in s_sleep 1 units (64 clocks)
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Sync words, each hot one on its own 128-byte line (pollers and updaters of
-// different words then never contend for one line).
-constexpr int kSlabs = 0, kFinishers = 32, kError = 64, kTiles = 96;
+// Sync words of the GEMM half of the counter header, each hot one on its own
+// 128-byte line (pollers and updaters of different words never share one).
+constexpr int kFinishers = 32, kError = 64, kEpoch = 96, kTiles = 128;
 
 struct SkinnyKArgs {
   const half_t* X;
@@ -44,164 +54,238 @@ struct SkinnyKArgs {
   const half_t* w_g;
   half_t* Y;
   int M, K, N, rank, KC, NBLK;
-  int T, S, CPS, P, ksp, R1p, ps;
+  int T, S, CPS, P, ksp, ps, r1p;
   int ec_mode;            // 0: no EC; 1: fused producers; 2: P and g given (split variant)
   float gate_bias, skip_tau;
-  uint32_t* sync;         // [kSlabs] slabs published, [kFinishers] finishers past the wait,
-                          // [kError] error, [kTiles + t] split-K tile counters
-  float* ec_part;         // [P][16][r1p4], r1p4 = rank + 1 rounded up to 4
+  uint32_t* sync;         // [kFinishers] GEMM workgroups done, [kError] error, [kEpoch] call
+                          // epoch, [kTiles + t] split-K tile counters
+  uint64_t* handoff;      // ec_mode 1: [P][M][r1p] slab sums of [P | z], each
+                          // (epoch + 1) << 32 | float bits
   float* gemm_part;       // [T*S][NBW][64][4]
   const float* Pext;      // ec_mode 2: [M][ps]
   const float* gext;      // ec_mode 2: [M]
   uint32_t spin_limit;
+  uint32_t stream_delay;  // ec_mode 1: s_sleep units before the weight stream (producers' head start)
 };
 
-// Direct global -> LDS copies (no VGPR result, so nothing waits on them until
-// the LDS is read).  For 2-byte copies lane L writes one dword at dst + 4 L
-// (the value zero-extended), for 16-byte copies 16 bytes at dst + 16 L.
-__device__ __forceinline__ void copy_to_lds_u16(const half_t* src, void* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)dst_wave_base, 2, 0, 0);
-}
+// Direct global -> LDS copy of 16 bytes per lane (lane L writes
+// dst + 16 L); no VGPR result, so nothing waits on it until the LDS is read.
 __device__ __forceinline__ void copy_to_lds_16b(const void* src, void* dst_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 16, 0, 0);
 }
-__device__ __forceinline__ half_t lds_half(const uint32_t* slot) {
-  return __builtin_bit_cast(half_t, (uint16_t)*slot);
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- producer
 //
-// A producer owns the K slab [k0, k0 + ksp) (ksp a power of two).  LDS:
-// As[ksp][rank] halves (the A slab, copied verbatim: it is contiguous in
-// memory), Wh[ksp] halves (the w_g slab), then red[4][kPass][64] float4 for
-// the sum over the four waves.  Copy regions are rounded up to whole 64-lane
-// copies so no copy spills over.  X fragments come straight from memory
-// through a buffer resource: rows >= M and k >= K read as zeros, so the
-// clamped (finite) A and w_g values past K contribute nothing.
+// Producer p owns the K slab [k0, k0 + ksp).  LDS: the A slab As[ksp][rank]
+// copied verbatim, the w_g slab Wh[ksp], the gate column Wg[ksp][4] (w_g in
+// column 0, zeros beside it), and the X slab Xs[16][ksp] whose 16-byte units
+// are XOR-swizzled by row (unit u of row r in slot u ^ (r % 16)), so the 16
+// rows of one fragment read hit 16 different bank groups.  B fragments of the
+// row-major A slab come from two transposing LDS reads (ds_read_b64_tr_b16):
+// within each 16-lane group, lane 4e + c supplies the address of
+// A[k + e][j + 4c .. j + 4c + 3], and lane i then holds A[k .. k + 3][j + i].
+// The gate block reads Wg the same way with row stride 4: its column 0 is
+// w_g, its other columns (finite neighbours) are never published.
 
-constexpr int kPass = 4;                 // column blocks per pass (16 columns each)
-constexpr int kMaxKbPerWave = 8;         // ksp <= 1024
+constexpr int kPass = 4;                 // column blocks per pass
+constexpr int kRedBytes = 4 * kPass * kWave * 16;   // the four waves' sums of one pass
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
+
+// Copy regions are rounded up to whole 64-lane copies so no copy spills over;
+// the A slab has 64 bytes of slack for the column tail of its last row.
+__host__ __device__ __forceinline__ int prod_a_units(int ksp, int rank) { return (ksp * rank / 8 + kWave - 1) / kWave * kWave; }
+__host__ __device__ __forceinline__ int prod_w_units(int ksp) { return (ksp / 8 + kWave - 1) / kWave * kWave; }
+// The four waves' sums of a pass (red) overlay the X slab when there is one
+// pass only (the slab is no longer read then), else follow it.
+__host__ __device__ __forceinline__ bool producer_red_own(int rank) { return (rank + 15) / 16 + 1 > kPass; }
+__host__ __device__ __forceinline__ size_t producer_xs_bytes(int ksp, int rank) {
+  const size_t xs = (size_t)16 * ksp * 2;
+  if (producer_red_own(rank)) return xs + kRedBytes;
+  return xs > (size_t)kRedBytes ? xs : (size_t)kRedBytes;
+}
+__host__ __device__ __forceinline__ size_t producer_lds_bytes(int ksp, int rank) {
+  return (size_t)prod_a_units(ksp, rank) * 16 + 64 + (size_t)prod_w_units(ksp) * 16 + (size_t)ksp * 8 + 64 +
+         producer_xs_bytes(ksp, rank);
+}
 
 struct ProducerLds {
   half_t* As;
   half_t* Wh;
-  float4_t* red;
+  half_t* Wg;
+  half_t* Xs;
 };
 
-__device__ __forceinline__ int prod_a_units(int ksp, int rank) { return (ksp * rank / 8 + kWave - 1) / kWave * kWave; }
-__device__ __forceinline__ int prod_w_units(int ksp) { return (ksp / 8 + kWave - 1) / kWave * kWave; }
-
-__device__ ProducerLds producer_lds(unsigned char* lds, int ksp, int rank) {
+__device__ ProducerLds producer_lds(unsigned char* base, int ksp, int rank) {
   ProducerLds L;
   size_t off = 0;
-  L.As = reinterpret_cast<half_t*>(lds + off);  off += (size_t)prod_a_units(ksp, rank) * 16;
-  L.Wh = reinterpret_cast<half_t*>(lds + off);  off += (size_t)prod_w_units(ksp) * 16;
-  L.red = reinterpret_cast<float4_t*>(lds + off);
+  L.As = reinterpret_cast<half_t*>(base + off);  off += (size_t)prod_a_units(ksp, rank) * 16 + 64;
+  L.Wh = reinterpret_cast<half_t*>(base + off);  off += (size_t)prod_w_units(ksp) * 16;
+  L.Wg = reinterpret_cast<half_t*>(base + off);  off += (size_t)ksp * 8 + 64;
+  L.Xs = reinterpret_cast<half_t*>(base + off);
   return L;
+}
+
+__device__ __forceinline__ half8_t lds_b_fragment_tr(const half_t* row0, int rank, int lane) {
+  // Lane 16 t + 4 e + c: rows 8 t + e (first read) and 8 t + 4 + e (second).
+  const int t = lane / 16, e = (lane % 16) / 4, c = lane % 4;
+  const half_t* p0 = row0 + (size_t)(8 * t + e) * rank + 4 * c;
+  const half4_t lo = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)p0));
+  const half4_t hi =
+      __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t*)(p0 + 4 * rank)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
   const int tid = threadIdx.x, lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int c16 = lane % 16, t4 = lane / 16;
   const int ksp = a.ksp;
   const int k0 = p * ksp;
   const int kn = min(ksp, a.K - k0);          // multiple of 8
   const int pblocks = (a.rank + 15) / 16;
-  const int r1 = a.rank + 1;
+  const int nblocks = pblocks + 1;            // the last block carries the gate logit
   const ProducerLds L = producer_lds(lds, ksp, a.rank);
+  const uint32_t tag = ld_dev_u32(&a.sync[kEpoch]) + 1u;   // needed only at the end
 
-  // A slab rows k0 .. k0+kn (kn*rank/8 16-byte units; A is 16-byte aligned
-  // and k0*rank*2 is a multiple of 16) and the w_g slab (kn/8 units; w_g is
-  // 16-byte aligned, k0*2 a multiple of 64).  Clamped units duplicate the
-  // last real unit.
+  // ---- slab copies, split over the four waves.  A slab rows k0 .. k0+kn
+  // (kn*rank/8 16-byte units; A is 16-byte aligned and k0*rank*2 is a
+  // multiple of 16) and the w_g slab; clamped units duplicate the last real
+  // unit.  X rows >= M and k >= K read as zeros.
   {
     const int nvec = kn * a.rank / 8;
     const u32x4_t* asrc = reinterpret_cast<const u32x4_t*>(a.A + (size_t)k0 * a.rank);
-    for (int base = wave * kWave; base < prod_a_units(ksp, a.rank); base += 4 * kWave)
+    for (int base = w * kWave; base < prod_a_units(ksp, a.rank); base += 4 * kWave)
       copy_to_lds_16b(asrc + min(base + lane, nvec - 1), L.As + (size_t)base * 8);
     const u32x4_t* wsrc = reinterpret_cast<const u32x4_t*>(a.w_g + k0);
-    for (int base = wave * kWave; base < prod_w_units(ksp); base += 4 * kWave)
+    for (int base = w * kWave; base < prod_w_units(ksp); base += 4 * kWave)
       copy_to_lds_16b(wsrc + min(base + lane, kn / 8 - 1), L.Wh + (size_t)base * 8);
-  }
-  // X fragments of this wave's k-blocks kb = wave, wave + 4, ...
-  const int kblocks = ksp / 32;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
-  half8_t xa[kMaxKbPerWave];
-#pragma unroll
-  for (int i = 0; i < kMaxKbPerWave; ++i) {
-    const int kb = wave + 4 * i;
-    const int k = k0 + kb * 32 + 8 * t4;
-    const bool live = kb < kblocks && c16 < a.M && k < a.K;
-    xa[i] = buffer_load_half8(xr, live ? (uint32_t)(c16 * a.K + k) * 2u : kOutOfRange);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
+    const int units = ksp / 8;                 // per row, >= 16
+    for (int idx = w * kWave; idx < 16 * units; idx += 4 * kWave) {
+      const int row = (idx + lane) / units, slot = (idx + lane) % units;
+      const int unit = slot ^ (row % 16);
+      const int k = k0 + unit * 8;
+      const uint32_t voff = (row < a.M && k < a.K) ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)k) * 2u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(L.Xs + (size_t)idx * 8), 16, voff, 0, 0, 0);
+    }
   }
   drain_vm();
   __syncthreads();
 
-  // Column blocks in passes of kPass: blocks 0 .. pblocks-1 hold P (columns
-  // >= rank clamped, never published); in the first pass, an extra block
-  // holds the gate logit in its column 0.  Each wave sums its k-blocks, then
-  // the four waves add up through LDS and publish rows 4 t4 .. 4 t4 + 3 of
-  // this slab's [P | z] (row stride r1p4 = rank + 1 rounded up to 4).
-  const int r1p4 = (r1 + 3) & ~3;
-  float* part = a.ec_part + (size_t)p * 16 * r1p4;
-  for (int nb0 = 0; nb0 < pblocks; nb0 += kPass) {
-    float4_t acc[kPass + 1];
+  // ---- gate column: Wg[k][0] = w_g[k0 + k], Wg[k][1..3] = 0 (and slack rows)
+  for (int k = tid; k < ksp + 8; k += kThreads) {
+    const half_t wv = k < ksp ? L.Wh[k] : (half_t)0.0f;
+    half4_t q = {wv, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
+    *reinterpret_cast<half4_t*>(L.Wg + (size_t)k * 4) = q;
+  }
+  __syncthreads();
+
+  // ---- wave w takes the 32-k blocks kb = w, w + 4, ... of the slab for
+  // every column block (P blocks, then the gate block), in passes of kPass
+  // blocks; the four waves' sums meet in LDS (red), and wave j stores block j
+  // of the pass.  Rows 4 t4 ..
+  // 4 t4 + 3 (< M) are published, columns >= rank of a P block are not.
+  // Nothing waits for the stores: the tags tell the readers when they landed.
+  uint64_t* slab = a.handoff + (size_t)p * a.M * a.r1p;
+  const int kbw = ksp / 32 / 4;                // 32-k blocks per wave
+  const half_t* xrow = L.Xs + (size_t)c16 * ksp;
+  float4_t* red = reinterpret_cast<float4_t*>(L.Xs + (producer_red_own(a.rank) ? (size_t)16 * ksp : 0));
+                                               // [4 waves][kPass][64 lanes]
+  for (int nb0 = 0; nb0 < nblocks; nb0 += kPass) {
+    const half_t* bsrc[kPass];
+    int bstride[kPass];
 #pragma unroll
-    for (int i = 0; i <= kPass; ++i) acc[i] = zero_float4();
-#pragma unroll
-    for (int i = 0; i < kMaxKbPerWave; ++i) {
-      const int kb = wave + 4 * i;
-      if (kb < kblocks) {
-        const int kk0 = kb * 32 + 8 * t4;
-#pragma unroll
-        for (int j = 0; j < kPass; ++j) {
-          if (nb0 + j < pblocks) {
-            const half_t* col = L.As + (size_t)kk0 * a.rank + min((nb0 + j) * 16 + c16, a.rank - 1);
-            half8_t b;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = col[e * a.rank];
-            acc[j] = mfma16x16x32(xa[i], b, acc[j]);
-          }
-        }
-        if (nb0 == 0) {
-          const half8_t wv = *reinterpret_cast<const half8_t*>(&L.Wh[kk0]);
-          acc[kPass] = mfma16x16x32(xa[i], c16 == 0 ? wv : zero_half8(), acc[kPass]);
-        }
-      }
+    for (int j = 0; j < kPass; ++j) {
+      const int blk = min(nb0 + j, nblocks - 1);   // past the last: computed, never stored
+      const bool gate = blk == pblocks;
+      bsrc[j] = gate ? L.Wg : L.As + blk * 16;
+      bstride[j] = gate ? 4 : a.rank;
     }
-    __syncthreads();   // previous pass is done with red
+    float4_t acc[kPass];
 #pragma unroll
-    for (int j = 0; j <= kPass; ++j) L.red[(wave * (kPass + 1) + j) * kWave + lane] = acc[j];
+    for (int j = 0; j < kPass; ++j) acc[j] = zero_float4();
+    for (int i = 0; i < kbw; ++i) {
+      const int kb = w + 4 * i;
+      const half8_t xf = *reinterpret_cast<const half8_t*>(xrow + (size_t)(((kb * 4 + t4) ^ c16) * 8));
+      half8_t bf[kPass];
+#pragma unroll
+      for (int j = 0; j < kPass; ++j)
+        bf[j] = lds_b_fragment_tr(bsrc[j] + (size_t)kb * 32 * bstride[j], bstride[j], lane);
+#pragma unroll
+      for (int j = 0; j < kPass; ++j) acc[j] = mfma16x16x32(xf, bf[j], acc[j]);
+    }
+    __syncthreads();                           // every wave is done with the X slab / last pass
+#pragma unroll
+    for (int j = 0; j < kPass; ++j) red[(w * kPass + j) * kWave + lane] = acc[j];
     __syncthreads();
-    for (int j = wave; j <= kPass; j += 4) {
-      const bool gate = j == kPass;
-      if (gate ? nb0 != 0 : nb0 + j >= pblocks) continue;
-      float4_t sum = L.red[j * kWave + lane];
+    const int blk = nb0 + w;
+    if (w < kPass && blk < nblocks) {
+      float4_t sum = red[(0 * kPass + w) * kWave + lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) sum += L.red[(w * (kPass + 1) + j) * kWave + lane];
-      const int col = gate ? a.rank : (nb0 + j) * 16 + c16;
+      for (int q = 1; q < 4; ++q) sum += red[(q * kPass + w) * kWave + lane];
+      const bool gate = blk == pblocks;
+      const int col = gate ? a.rank : blk * 16 + c16;
       if (gate ? c16 == 0 : col < a.rank) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) st_dev(&part[(4 * t4 + v) * r1p4 + col], sum[v]);
+        for (int v = 0; v < 4; ++v)
+          if (4 * t4 + v < a.M)
+            st_dev_u64(&slab[(size_t)(4 * t4 + v) * a.r1p + col], ((uint64_t)tag << 32) | float_bits(sum[v]));
       }
     }
   }
-  // Publish: drain the stores, then count this slab in.
-  drain_vm();
-  __syncthreads();
-  if (tid == 0) add_dev_u32(&a.sync[kSlabs], 1u);
 }
 
 // ---------------------------------------------------------------- GEMM tile
 
+// Static LDS of a GEMM workgroup: the sums of waves 1..3, then flags and the
+// block-wide vote's word (512 bytes of room).
+constexpr size_t static_lds_bytes(int nbw) { return (size_t)3 * kWave * nbw * 16 + 512; }
+
+// Dynamic LDS of a GEMM workgroup with the EC on: the EC factor tile
+// Bs[jblocks*32][TN] (fp16); Pc[16][rank + 1] floats (P, then the final gate
+// g'); then the fused variant's copy of the hand-off slabs Ht[P][M][r1p] or
+// the split variant's Pt[16][ps] floats and gt[16].
+//
+// The EC operands are loaded into registers, a fixed number per thread, with
+// straight-line code: the B tile and the split variant's P and g ahead of the
+// weight stream (they are ready), the hand-off slabs right behind it.  (With
+// a loop, or with a direct-to-LDS copy, among these loads the compiler can no
+// longer count the loads in flight, and it waits for all of them before the
+// first matrix instruction.)  Whatever these do not cover is loaded after the
+// matrix instructions.
+constexpr int kBLoads = 4;    // B tile halves per thread
+constexpr int kPLoads = 1;    // split: 16-byte units of P per thread
+constexpr int kHLoads = 4;    // fused: 16-byte hand-off units (two entries) per thread
+constexpr int kHCovered = kHLoads * kThreads;   // 16-byte units loaded ahead
+__host__ __device__ __forceinline__ size_t gemm_bs_bytes(int ps, int tn) {
+  return ((size_t)ps * tn * 2 + 15) & ~(size_t)15;
+}
+__host__ __device__ __forceinline__ size_t gemm_pc_bytes(int rank) { return ((size_t)16 * (rank + 1) * 4 + 15) & ~(size_t)15; }
+__host__ __device__ __forceinline__ size_t gemm_table_bytes(int ec_mode, int ps, int r1p, int P, int M) {
+  if (ec_mode == 1) {
+    const size_t need = (size_t)P * M * r1p * 8, ahead = (size_t)kHCovered * 16;
+    return need > ahead ? need : ahead;
+  }
+  return (size_t)16 * ps * 4 + 16 * 4;
+}
+
 // EXACT: every wave owns exactly CPW chunks (no validity test, so no load
-// ends up under a branch).
-template <int NBW, int CPW, bool EXACT>
+// ends up under a branch).  ECM: the EC mode (0 none, 1 fused, 2 split), fixed
+// at compile time so the loads of each mode are straight-line code.
+template <int NBW, int CPW, bool EXACT, int ECM>
 __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   __shared__ float4_t red[3][kWave][NBW];
-  if ((int)blockIdx.x < a.P) {
+  __shared__ uint32_t flags[2];        // [1] last split
+  if (ECM == 1 && (int)blockIdx.x < a.P) {
     ec_producer(a, dyn_lds, blockIdx.x);
     return;
   }
@@ -215,12 +299,48 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
   const int wbeg = cbeg + w * CPW;
   const int nb0 = t * NBW;
   const int n0 = nb0 * 16;
-  const int jblocks = a.ec_mode ? a.ps / 32 : 0;
+  const int jblocks = ECM ? a.ps / 32 : 0;
   const int r1 = a.rank + 1;
-  // LDS of a GEMM workgroup: the EC factor tile Bs[jblocks*32][TN] (one dword
-  // per value, fp16 in the low half), then Pc[16][rank + 1] floats (P and z).
-  uint32_t* Bs = reinterpret_cast<uint32_t*>(dyn_lds);
-  float* Pc = reinterpret_cast<float*>(Bs + jblocks * 32 * TN);
+  half_t* Bs = reinterpret_cast<half_t*>(dyn_lds);
+  float* Pc = reinterpret_cast<float*>(dyn_lds + gemm_bs_bytes(a.ps, TN));
+  unsigned char* table = dyn_lds + gemm_bs_bytes(a.ps, TN) + gemm_pc_bytes(a.rank);
+  // The epoch is read before the weight stream is requested, so it returns
+  // ahead of it.
+  const uint32_t tag = ECM == 1 ? ld_dev_u32(&a.sync[kEpoch]) + 1u : 0u;
+
+  // ---- EC operands that are ready now, ahead of the weight stream: the B
+  // tile (element q = row * TN + column; rows >= rank and columns >= N
+  // clamped: they meet zero P columns or are never stored) and, split
+  // variant, the given P (16-byte units of the [M][ps] table) and g.
+  const int brows = jblocks * 32;
+  half_t breg[kBLoads];
+  if (ECM) {
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) {
+      const int q = i * kThreads + tid;
+      const int row = min(q / TN, a.rank - 1), col = min(n0 + q % TN, a.N - 1);
+      breg[i] = a.Bec[(size_t)row * a.N + col];
+    }
+  }
+  float4_t preg[kPLoads];
+  float greg = 0.0f;
+  const int p_units = ECM == 2 ? a.M * a.ps / 4 : 0;
+  if (ECM == 2) {
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.Pext, (uint32_t)((size_t)a.M * a.ps * 4));
+#pragma unroll
+    for (int i = 0; i < kPLoads; ++i) {
+      const int u = i * kThreads + tid;
+      preg[i] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  pr, u < p_units ? (uint32_t)u * 16u : kOutOfRange, 0, 0));
+    }
+    greg = a.gext[min(tid, a.M - 1)];
+  }
+
+  // Fused: the producers' loads go first (their CUs carry no weight stream,
+  // but the memory channels are shared).
+  if (ECM == 1) {
+    for (uint32_t i = 0; i < a.stream_delay; ++i) __builtin_amdgcn_s_sleep(1);
+  }
 
   // Scales of this lane's columns (columns >= N are clamped, never stored).
   half_t scr[NBW];
@@ -228,7 +348,7 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
   for (int nb = 0; nb < NBW; ++nb) scr[nb] = a.scales[min(n0 + nb * 16 + c16, a.N - 1)];
 
   // ---- issue every load of this wave's K range.  Chunk validity is uniform
-  // over the wave; X rows >= M are clamped (their outputs are never stored).
+  // over the wave.
   u32x4_t bw[CPW][NBW];
   half8_t xa[CPW][4];
   // X through a buffer resource: lanes of rows >= M read out of range, which
@@ -253,7 +373,21 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
       for (int j = 0; j < 4; ++j) xa[c][j] = zero_half8();
     }
   }
-  // Keep every stream load above this point (no load may sink into the
+  // ---- fused: the hand-off slabs behind the weight stream (device-coherent
+  // loads; units past the table read as zeros, tag 0).
+  const int handoff_units = ECM == 1 ? a.P * a.M * a.r1p / 2 : 0;   // 16-byte units, two entries each
+  u32x4_t hreg[kHLoads];
+  if (ECM == 1) {
+    const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.handoff, (uint32_t)((size_t)handoff_units * 16));
+#pragma unroll
+    for (int i = 0; i < kHLoads; ++i) {
+      const int u = i * kThreads + tid;
+      hreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                hr, u < handoff_units ? (uint32_t)u * 16u : kOutOfRange, 0,
+                                                kCachePolicySc1));
+    }
+  }
+  // Keep every load above this point (no load may sink into the
   // matrix-instruction block and pay a second round trip).
   __builtin_amdgcn_sched_barrier(0);
 
@@ -268,22 +402,38 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) acc[nb] = mfma16x16x32(xa[c][j], decode_w4(bw[c][nb][j]), acc[nb]);
 
-  // EC factor tile B[0 .. jblocks*32) x [n0, n0 + TN) -> Bs, straight to LDS.
-  // Rows >= rank are clamped (they meet zero P columns).  Issued after the
-  // main matrix instructions: a direct-to-LDS copy among the stream loads
-  // would make every wait a full drain, and its latency hides behind the EC
-  // wait anyway.
-  if (jblocks > 0) {
-    constexpr int kRowsPerCopy = kWave / TN;          // 1, 2 or 4
-    const int rows = jblocks * 32;
-    for (int r0 = w * kRowsPerCopy; r0 < rows; r0 += 4 * kRowsPerCopy) {
-      const int row = min(r0 + lane / TN, a.rank - 1);
-      const int col = min(n0 + lane % TN, a.N - 1);
-      copy_to_lds_u16(a.Bec + (size_t)row * a.N + col, Bs + r0 * TN);
+  // ---- EC operands -> LDS (then what the registers did not cover)
+  if (ECM) {
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) {
+      const int q = i * kThreads + tid;
+      if (q < brows * TN) Bs[q] = breg[i];
+    }
+    for (int q = kBLoads * kThreads + tid; q < brows * TN; q += kThreads) {
+      const int row = min(q / TN, a.rank - 1), col = min(n0 + q % TN, a.N - 1);
+      Bs[q] = a.Bec[(size_t)row * a.N + col];
     }
   }
+  if (ECM == 1) {
+#pragma unroll
+    for (int i = 0; i < kHLoads; ++i) {
+      const int u = i * kThreads + tid;
+      if (u < handoff_units) reinterpret_cast<u32x4_t*>(table)[u] = hreg[i];
+    }
+  }
+  if (ECM == 2) {
+    float4_t* Pt4 = reinterpret_cast<float4_t*>(table);
+#pragma unroll
+    for (int i = 0; i < kPLoads; ++i) {
+      const int u = i * kThreads + tid;
+      if (u < p_units) Pt4[u] = preg[i];
+    }
+    for (int u = kPLoads * kThreads + tid; u < p_units; u += kThreads)
+      Pt4[u] = reinterpret_cast<const float4_t*>(a.Pext)[u];
+    if (tid < a.M) reinterpret_cast<float*>(table + (size_t)16 * a.ps * 4)[tid] = greg;
+  }
 
-  // ---- four waves -> wave 0 (the drain and barrier also publish the Bs copies)
+  // ---- four waves -> wave 0
   if (w > 0) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) red[w - 1][lane][nb] = acc[nb];
@@ -297,9 +447,9 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
       for (int nb = 0; nb < NBW; ++nb) acc[nb] += red[i][lane][nb];
   }
 
-  // ---- S splits -> the last to arrive (wave 0 exchanges, the block follows)
+  // ---- S splits -> the last to arrive (wave 0 exchanges, the block follows).
+  // Workgroups that are not last count themselves out and leave.
   if (a.S > 1) {
-    __shared__ uint32_t last_s;
     if (w == 0) {
       float* slot = a.gemm_part + ((size_t)(t * a.S + s) * NBW) * kWave * 4;
 #pragma unroll
@@ -307,10 +457,19 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) st_dev(&slot[(nb * kWave + lane) * 4 + v], acc[nb][v]);
       drain_vm();
-      if (lane == 0) last_s = (add_dev_u32(&a.sync[kTiles + t], 1u) == (uint32_t)(a.S - 1)) ? 1u : 0u;
+      if (lane == 0) flags[1] = (add_dev_u32(&a.sync[kTiles + t], 1u) == (uint32_t)(a.S - 1)) ? 1u : 0u;
     }
     __syncthreads();
-    if (!last_s) return;
+    if (!flags[1]) {
+      if (ECM == 1 && tid == 0) {
+        const uint32_t before = add_dev_u32(&a.sync[kFinishers], 1u);
+        if (before == (uint32_t)(a.T * a.S - 1)) {
+          st_dev_u32(&a.sync[kFinishers], 0u);
+          st_dev_u32(&a.sync[kEpoch], tag);
+        }
+      }
+      return;
+    }
     if (w == 0) {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) acc[nb] = zero_float4();
@@ -325,76 +484,115 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
     }
   }
 
-  // ---- EC projection of the 16 rows -> Pc (all four waves): wait until the
-  // P slabs are published, then add them in fixed order.  The finisher count
-  // is bumped right after the wait; its result (last finisher resets the
-  // counters) is needed only at the very end.
-  uint32_t finishers_before = 0;
-  if (a.ec_mode == 1) {
-    if (tid == 0) {
-      uint32_t n = 0;
-      while (ld_dev_u32(&a.sync[kSlabs]) < (uint32_t)a.P) {
-        if (++n > a.spin_limit) { st_dev_u32(&a.sync[kError], 1u); break; }
-        __builtin_amdgcn_s_sleep(8);
+  // ---- fused: complete the hand-off copy and check its tags; units that
+  // were not yet published are reloaded (bounded wait).
+  if (ECM == 1) {
+    uint64_t* Ht = reinterpret_cast<uint64_t*>(table);
+    u32x4_t* Hu = reinterpret_cast<u32x4_t*>(table);
+    const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.handoff, (uint32_t)((size_t)handoff_units * 16));
+    // A unit (two entries) is ready when every entry of it that the producers
+    // write (columns < rank + 1) carries this call's tag.
+    auto unit_ready = [&](const u32x4_t& v, int u) {
+      const int e0 = 2 * u;
+      const bool ok0 = e0 % a.r1p >= r1 || v[1] == tag;
+      const bool ok1 = (e0 + 1) % a.r1p >= r1 || v[3] == tag;
+      return ok0 && ok1;
+    };
+    // Units past the registers' reach: one batch of loads now.
+    for (int u0 = kHCovered; u0 < handoff_units; u0 += 8 * kThreads) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int u = u0 + i * kThreads + tid;
+        v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               hr, u < handoff_units ? (uint32_t)u * 16u : kOutOfRange, 0,
+                                               kCachePolicySc1));
       }
-      finishers_before = add_dev_u32(&a.sync[kFinishers], 1u);
-    }
-    __syncthreads();
-    const int r1p4 = (r1 + 3) & ~3, u4 = r1p4 / 4;
-    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.ec_part, (uint32_t)((size_t)a.P * 16 * r1p4 * 4));
-    for (int unit = tid; unit < 16 * u4; unit += kThreads) {
-      float4_t sum = zero_float4();
-      for (int p0 = 0; p0 < a.P; p0 += 8) {
-        float4_t v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          v[q] = buffer_load_f4_dev(pr, (uint32_t)((min(p0 + q, a.P - 1) * 16 * u4 + unit) * 16));
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (p0 + q < a.P) sum += v[q];
+      for (int i = 0; i < 8; ++i) {
+        const int u = u0 + i * kThreads + tid;
+        if (u < handoff_units) Hu[u] = v[i];
       }
-      const int row = unit / u4, c0 = (unit % u4) * 4;
+    }
+    // Units not yet published: reload, up to sixteen at a time per thread,
+    // until ready (bounded).
+    uint32_t n = 0;
+    for (;;) {
+      bool stale = false;
+      int pend[16];
+      int np = 0;
+      for (int u = tid; u < handoff_units && np < 16; u += kThreads)
+        if (!unit_ready(Hu[u], u)) pend[np++] = u;
+      stale = np > 0;
+      if (!__syncthreads_or(stale)) break;
+      if (++n > a.spin_limit) {
+        if (tid == 0) st_dev_u32(&a.sync[kError], 1u);
+        break;
+      }
+      if (np > 0) {
+        if (n > 1) __builtin_amdgcn_s_sleep(4);
+        u32x4_t v[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (c0 + e < r1) Pc[row * r1 + c0 + e] = sum[e];
+        for (int i = 0; i < 16; ++i)
+          v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 hr, i < np ? (uint32_t)pend[i] * 16u : kOutOfRange, 0,
+                                                 kCachePolicySc1));
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (i < np) Hu[pend[i]] = v[i];
+      }
+    }
+    // Add the slabs in fixed order into Pc, with the gate applied.
+    for (int idx = tid; idx < a.M * r1; idx += kThreads) {
+      const int row = idx / r1, col = idx % r1;
+      float v = 0.0f;
+      for (int p = 0; p < a.P; ++p)
+        v += bits_float((uint32_t)Ht[((size_t)p * a.M + row) * a.r1p + col]);
+      if (col == a.rank) {
+        v = sigmoidf_(v + a.gate_bias);
+        if (a.skip_tau > 0.0f && !(v >= a.skip_tau)) v = 0.0f;
+      }
+      Pc[idx] = v;
     }
     __syncthreads();
-  } else if (a.ec_mode == 2) {
-    for (int idx = tid; idx < 16 * r1; idx += kThreads) {
-      const int row = min(idx / r1, a.M - 1), col = idx % r1;
-      Pc[idx] = col < a.rank ? a.Pext[(size_t)row * a.ps + col] : a.gext[row];
+    // Count this workgroup out (wave 1, off wave 0's path): the last one
+    // returns the counters to zero and advances the epoch (every producer and
+    // every reader is done by then).
+    if (tid == kWave) {
+      const uint32_t before = add_dev_u32(&a.sync[kFinishers], 1u);
+      if (before == (uint32_t)(a.T * a.S - 1)) {
+        st_dev_u32(&a.sync[kFinishers], 0u);
+        st_dev_u32(&a.sync[kEpoch], tag);
+      }
     }
-    __syncthreads();
   }
   if (w > 0) return;
 
   // ---- gated EC epilogue (wave 0)
+  auto ec_value = [&](int row, int col) -> float {   // P (col < rank) or g (col == rank)
+    if (ECM == 1) return Pc[row * r1 + col];
+    const float* Pt = reinterpret_cast<const float*>(table);
+    if (col < a.rank) return Pt[row * a.ps + col];
+    return reinterpret_cast<const float*>(table + (size_t)16 * a.ps * 4)[row];
+  };
   float4_t ec[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) ec[nb] = zero_float4();
-  if (a.ec_mode) {
-    float gv = 0.0f;
-    if (c16 < a.M) {
-      if (a.ec_mode == 1) {
-        gv = sigmoidf_(Pc[c16 * r1 + a.rank] + a.gate_bias);
-        if (a.skip_tau > 0.0f && !(gv >= a.skip_tau)) gv = 0.0f;
-      } else {
-        gv = Pc[c16 * r1 + a.rank];          // the split variant's gate, already final
-      }
-    }
+  if (ECM) {
+    const float gv = c16 < a.M ? ec_value(c16, a.rank) : 0.0f;   // the final gate g'
     if (__any(gv != 0.0f)) {
       for (int jb = 0; jb < jblocks; ++jb) {
         half8_t pa;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int col = jb * 32 + 8 * t4 + e;
-          pa[e] = col < a.rank ? (half_t)(gv * Pc[c16 * r1 + col]) : (half_t)0.0f;
+          pa[e] = (col < a.rank && gv != 0.0f) ? (half_t)(gv * ec_value(c16, col)) : (half_t)0.0f;
         }
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
           half8_t bb;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bb[e] = lds_half(&Bs[(jb * 32 + 8 * t4 + e) * TN + nb * 16 + c16]);
+          for (int e = 0; e < 8; ++e) bb[e] = Bs[(jb * 32 + 8 * t4 + e) * TN + nb * 16 + c16];
           ec[nb] = mfma16x16x32(pa, bb, ec[nb]);
         }
       }
@@ -414,24 +612,38 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
       }
     }
   }
+}
 
-  // The last finisher past the wait resets the counters for the next call
-  // (every finisher has seen all slabs by then).
-  if (a.ec_mode == 1 && lane == 0 && finishers_before == (uint32_t)(a.T - 1)) {
-    st_dev_u32(&a.sync[kSlabs], 0u);
-    st_dev_u32(&a.sync[kFinishers], 0u);
+// Let a kernel use all of a workgroup's LDS beside its static LDS (once per
+// instantiation).
+template <auto Kernel, int NBW>
+hipError_t allow_full_lds() {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)(kMaxLdsBytes - static_lds_bytes(NBW)));
+  return e;
+}
+
+template <int NBW, int CPW, bool EXACT>
+hipError_t launch_exact(const SkinnyKArgs& k, size_t lds, void* stream) {
+  const dim3 grid(k.P + k.T * k.S), block(kThreads);
+  hipError_t e = hipSuccess;
+  if (k.ec_mode == 1) {
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 1>, NBW>();
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 1>), grid, block, lds, (hipStream_t)stream, k);
+  } else if (k.ec_mode == 2) {
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 2>, NBW>();
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 2>), grid, block, lds, (hipStream_t)stream, k);
+  } else {
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 0>, NBW>();
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 0>), grid, block, lds, (hipStream_t)stream, k);
   }
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 template <int NBW, int CPW>
 hipError_t launch_nbw_cpw(const SkinnyKArgs& k, bool exact, size_t lds, void* stream) {
-  if (exact)
-    hipLaunchKernelGGL((skinny_kernel<NBW, CPW, true>), dim3(k.P + k.T * k.S), dim3(kThreads), lds,
-                       (hipStream_t)stream, k);
-  else
-    hipLaunchKernelGGL((skinny_kernel<NBW, CPW, false>), dim3(k.P + k.T * k.S), dim3(kThreads), lds,
-                       (hipStream_t)stream, k);
-  return hipGetLastError();
+  return exact ? launch_exact<NBW, CPW, true>(k, lds, stream) : launch_exact<NBW, CPW, false>(k, lds, stream);
 }
 
 constexpr int kMaxCpw = 8;   // chunks per wave kept in flight (NBW <= 2)
@@ -454,8 +666,8 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
                          size_t scratch_base) {
   SkinnyShape sh;
   const int64_t KC = k_pad(K) / kKChunk, NBLK = n_pad(N) / kNBlock;
-  // Candidates (panels per workgroup, K splits).  Preferred: a grid of at
-  // least one workgroup per CU; then "exact" ranges (every wave owns CPW =
+  // Candidates (panels per workgroup, K splits).  Preferred: the most
+  // workgroups up to one per CU; then "exact" ranges (every wave owns CPW =
   // CPS / 4 chunks); then the fewest splits (each split adds a round trip of
   // partial sums); then the widest tiles (least re-reading of X).
   int64_t best_score = -1;
@@ -469,8 +681,7 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
       if (CPW > max_cpw) continue;
       const bool exact = CPS == 4 * CPW && CPS * S == KC && (CPW == 1 || CPW == 2 || CPW == 4 || CPW == 8);
       const int64_t wgs = T * S;
-      const bool fills = wgs >= cus;
-      const int64_t score = (fills ? 1LL << 40 : wgs << 20) + (exact ? 1LL << 30 : 0) +
+      const int64_t score = (std::min<int64_t>(wgs, cus) << 32) + (exact ? 1LL << 30 : 0) +
                             ((64 - S) << 8) + nbw;
       if (score > best_score) {
         best_score = score;
@@ -480,34 +691,35 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
   }
   // Round CPW up to an instantiated value.
   sh.CPW = sh.CPW <= 1 ? 1 : sh.CPW <= 2 ? 2 : sh.CPW <= 4 ? 4 : 8;
+  const int ps = rank > 0 ? (int)p_stride(rank) : 0;
+  const int r1p = (int)round_up(rank + 1, 2);
   if (fused && rank > 0) {
-    // Producer slabs: a power of two near K / 4 (32 .. 1024), halved until one
-    // slab's LDS (A slab, w_g slab, four-wave sums) fits 64 KiB, and doubled
-    // (up to 1024) while there would be more than 64 slabs.
-    int64_t ksp = 32;
-    while (ksp < 1024 && ksp * 4 < K) ksp *= 2;
-    auto lds_of = [&](int64_t k) {
-      return round_up(k * rank / 8, kWave) * 16 + round_up(k / 8, kWave) * 16 + 4 * 5 * kWave * 16;
-    };
-    while (ksp > 32 && lds_of(ksp) > 64 * 1024) ksp /= 2;
-    while (ksp < 1024 && ceil_div(K, ksp) > 64) ksp *= 2;
+    // Producer slabs: a power of two near K / 8 (128 .. 1024), halved until
+    // one slab's LDS (A slab, w_g slab and column, X slab) fits 64 KiB, so two
+    // workgroups fit a CU (every workgroup of the launch gets this LDS).
+    // Few slabs keep the hand-off that every GEMM workgroup reads small.
+    int64_t ksp = 128;
+    while (ksp < 1024 && ksp * 8 < K) ksp *= 2;
+    while (ksp > 128 && producer_lds_bytes((int)ksp, (int)rank) > 64 * 1024) ksp /= 2;
     sh.ksp = (int)ksp;
     sh.P = (int)ceil_div(K, ksp);
-    sh.lds = (size_t)lds_of(ksp);
+    sh.lds = producer_lds_bytes((int)ksp, (int)rank);
   }
-  if (rank > 0) {
-    // EC factor tile and the 16 projected rows of a GEMM workgroup.
-    sh.lds_gemm = (size_t)(p_stride(rank) * sh.nbw * 16 * 4 + 16 * (rank + 1) * 4);
-  }
-  // Workspace: sync words [4 + T] in the counter header; EC partials and the
-  // GEMM slots as scratch from scratch_base on.
+  if (rank > 0)
+    sh.lds_gemm = gemm_bs_bytes(ps, sh.nbw * 16) + gemm_pc_bytes((int)rank) +
+                  gemm_table_bytes(fused ? 1 : 2, ps, r1p, sh.P, (int)M);
+  // Workspace: sync words in the counter header and the hand-off slabs in the
+  // header's hand-off region; the split-K slots as scratch from scratch_base
+  // on.
   size_t off = scratch_base;
   auto take = [&](size_t bytes) { size_t o = off; off = (size_t)round_up((int64_t)(off + bytes), 256); return o; };
   sh.ws_sync = kGemmSyncOffset;
-  if (sh.P > 0) sh.ws_ec_part = take(sizeof(float) * (size_t)sh.P * 16 * (size_t)round_up(rank + 1, 4));
+  sh.ws_handoff = kHandoffOffset;
   if (sh.S > 1) sh.ws_gemm_part = take(sizeof(float) * 4 * kWave * (size_t)sh.nbw * sh.T * sh.S);
-  sh.ws_bytes = (sh.S > 1 || sh.P > 0) ? off : 0;
-  sh.sync_ok = kTiles + sh.T <= kMaxSyncWords;
+  sh.ws_bytes = (sh.S > 1 || sh.P > 0) ? (off > kSyncHeaderBytes ? off : kSyncHeaderBytes) : 0;
+  const size_t lds_room = kMaxLdsBytes - static_lds_bytes(sh.nbw);
+  sh.fits = kTiles + sh.T <= kMaxSyncWords && sh.lds <= lds_room && sh.lds_gemm <= lds_room &&
+            (size_t)sh.P * M * r1p * 8 <= kHandoffBytes;
   (void)M;
   return sh;
 }
@@ -528,17 +740,18 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream) {
   k.T = sh.T; k.S = sh.S; k.CPS = sh.CPS;
   k.P = L.ec_mode == 1 ? sh.P : 0;
   k.ksp = sh.ksp;
-  k.R1p = L.rank > 0 ? (int)ec_cols(L.rank) : 0;
   k.ps = L.ec_mode ? (int)p_stride(L.rank) : 0;
+  k.r1p = (int)round_up(L.rank + 1, 2);
   k.ec_mode = L.ec_mode;
   k.gate_bias = L.gate_bias; k.skip_tau = L.skip_tau;
   char* ws = (char*)L.workspace;
   k.sync = (uint32_t*)(ws + sh.ws_sync);   // absolute offsets from the workspace base
-  k.ec_part = (float*)(ws + sh.ws_ec_part);
+  k.handoff = (uint64_t*)(ws + sh.ws_handoff);
   k.gemm_part = (float*)(ws + sh.ws_gemm_part);
   k.Pext = L.Pext;
   k.gext = L.gext;
   k.spin_limit = 1u << 20;   // ~0.5 s of polling: far beyond any healthy wait
+  k.stream_delay = L.ec_mode == 1 ? kStreamDelay : 0;
   size_t lds = k.P > 0 ? sh.lds : 0;
   if (L.ec_mode && sh.lds_gemm > lds) lds = sh.lds_gemm;
   const bool exact = sh.CPS == 4 * sh.CPW && (int64_t)sh.CPS * sh.S == k.KC;
