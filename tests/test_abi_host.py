@@ -85,8 +85,11 @@ def test_dispatch_rules(lib):
     assert st == 0 and p.variant == 2
     st, p = plan(lib, 64, 4096, 4096, 32, variant=1)
     assert st == 3                        # the fused variant is built for M <= 16
+    st, p = plan(lib, 2048, 4096, 14336, 32, variant=3)
+    assert st == 0 and p.variant == 3 and p.split_k == 1 and p.workspace_bytes == 0
+    # mid-size M: 64-row tiles with K split over workgroups (partials in the workspace)
     st, p = plan(lib, 64, 4096, 4096, 32, variant=3)
-    assert st == 0 and p.variant == 3 and p.workspace_bytes == 0
+    assert st == 0 and p.variant == 3 and p.tile_m == 64 and p.split_k > 1 and p.workspace_bytes > 0
     st, p = plan(lib, 0, 512, 512, 16)
     assert st == 0
     assert p.abi_version == 1 and p.layout_id == 2 and p.cus == 256

@@ -199,6 +199,8 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.X = X; ga.Wq = Wq; ga.scales = scales; ga.Y = Y;
+  ga.workspace = workspace;
+  ga.scratch_base = ec_bytes ? ec_bytes : kSyncHeaderBytes;
   ga.M = desc->M; ga.K = desc->K; ga.N = desc->N; ga.rank = desc->rank;
   if (ec) {
     ga.B = B;

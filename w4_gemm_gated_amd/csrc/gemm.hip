@@ -21,6 +21,13 @@
 //     done with stage s-1, whose buffer the copies for step s+1 then refill.
 // Tiles are ordered so that the workgroups of one row of tiles run on one XCD
 // (blocks are dealt round-robin to the 8 XCDs), keeping that X row in one L2.
+//
+// When the tiles alone do not fill the GPU (mid-size M), K is split over S
+// workgroups per tile: each stores its fp32 partial tile (device-coherent
+// 16-byte stores) and takes a ticket; the last to arrive adds the S partials
+// in fixed order, so results do not depend on timing, and runs the epilogue.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -44,6 +51,9 @@ struct GemmKArgs {
   half_t* Y;
   int M, K, N, rank, KC, NBLK, ps, ec;
   int MT, NT;             // row and column tiles
+  int S, CPS;             // K splits, 128-k chunks per split
+  float* part;            // [tile][S][MBW * NBW][256 threads] float4 partials
+  uint32_t* tickets;      // [tile] split counters (back to zero after each call)
 };
 
 __device__ __forceinline__ void copy16_to_lds(const void* src, void* dst_wave_base) {
@@ -53,15 +63,15 @@ __device__ __forceinline__ void copy2_to_lds(const void* src, void* dst_wave_bas
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 2, 0, 0);
 }
 
-// Wave tile MBW x NBW blocks of 16 x 16; workgroup WM x WN waves.
-template <int MBW, int NBW, int WM, int WN>
+// Wave tile MBW x NBW blocks of 16 x 16; workgroup WM x WN waves.  SPLIT:
+// K split over a.S workgroups per tile.
+template <int MBW, int NBW, int WM, int WN, bool SPLIT>
 __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a) {
   static_assert(WM * WN * kWave == kGemmThreads, "four waves");
   constexpr int TM = 16 * MBW * WM;
   constexpr int TN = 16 * NBW * WN;
   constexpr int kStageHalves = TM * kKt;                    // one X stage
   constexpr int kCopiesPerWave = TM * kUnitsPerRow / kWave / 4;
-  static_assert(kEcChunk * TN * 4 + TM * kEcChunk * 2 <= 2 * TM * kKt * 2, "EC chunk fits the X stages");
   extern __shared__ __align__(16) unsigned char lds[];
   half_t* xs = reinterpret_cast<half_t*>(lds);                // [2][TM][kKt], swizzled units
 
@@ -73,8 +83,10 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
   // Tile order: with a multiple of 8 row tiles, XCD x (block % 8) takes row
   // tiles x, x + 8, ... and walks the column tiles of each.
   int m_tile, n_tile;
+  const int tiles = a.MT * a.NT;
+  const int split = blockIdx.x / tiles;
   {
-    const int bid = blockIdx.x;
+    const int bid = blockIdx.x % tiles;
     if (a.MT % 8 == 0) {
       const int xcd = bid % 8, j = bid / 8;
       m_tile = xcd + 8 * (j / a.NT);
@@ -122,13 +134,14 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
     for (int j = 0; j < NBW; ++j) acc[i][j] = zero_float4();
 
   u32x4_t wcur[NBW], wnext[NBW];
-  issue_x(0, 0);
-  load_w(0, wcur);
-  for (int kc = 0; kc < a.KC; ++kc) {
-    const int st = kc & 1;
+  const int kc_begin = split * a.CPS, kc_end = min(a.KC, kc_begin + a.CPS);
+  issue_x(kc_begin, 0);
+  load_w(kc_begin, wcur);
+  for (int kc = kc_begin; kc < kc_end; ++kc) {
+    const int st = (kc - kc_begin) & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kc + 1 < a.KC) {
+    if (kc + 1 < kc_end) {
       issue_x(kc + 1, st ^ 1);
       load_w(kc + 1, wnext);
     }
@@ -151,6 +164,41 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
     }
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) wcur[nb] = wnext[nb];
+  }
+
+  // ---------------------------------------------------------------- split K
+  if (SPLIT && a.S > 1) {
+    __shared__ uint32_t ticket;
+    const int tile = m_tile * a.NT + n_tile;
+    const uint32_t slice = (uint32_t)MBW * NBW * kGemmThreads * 16;   // bytes of one partial
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, (uint32_t)((size_t)tiles * a.S * slice));
+    const uint32_t own = (uint32_t)(tile * a.S + split) * slice;
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mb][nb]), pr,
+                                               own + (uint32_t)((mb * NBW + nb) * kGemmThreads + tid) * 16u, 0,
+                                               kCachePolicySc1);
+    drain_vm();
+    __syncthreads();
+    if (tid == 0) ticket = add_dev_u32(&a.tickets[tile], 1u);
+    __syncthreads();
+    if (ticket != (uint32_t)(a.S - 1)) return;
+    if (tid == 0) st_dev_u32(&a.tickets[tile], 0u);
+    // Fixed order: every partial, this workgroup's own included, from memory.
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = zero_float4();
+    for (int sp = 0; sp < a.S; ++sp) {
+      const uint32_t base = (uint32_t)(tile * a.S + sp) * slice;
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+          acc[mb][nb] += buffer_load_f4_dev(pr, base + (uint32_t)((mb * NBW + nb) * kGemmThreads + tid) * 16u);
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -233,33 +281,63 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
 }
 
 template <int MBW, int NBW, int WM, int WN>
-hipError_t launch_cfg(GemmKArgs k, void* stream) {
-  constexpr int TM = 16 * MBW * WM, TNB = NBW * WN;
-  k.MT = (int)ceil_div(k.M, TM);
-  k.NT = (int)ceil_div(k.NBLK, TNB);
-  const size_t lds = (size_t)2 * TM * kKt * 2;
+constexpr size_t tile_lds_bytes() {
+  constexpr int TM = 16 * MBW * WM, TN = 16 * NBW * WN;
+  constexpr size_t stages = (size_t)2 * TM * kKt * 2;
+  constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2;
+  return stages > epilogue ? stages : epilogue;
+}
+
+template <int MBW, int NBW, int WM, int WN, bool SPLIT>
+hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
+  constexpr size_t lds = tile_lds_bytes<MBW, NBW, WM, WN>();
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN>),
+      reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN>), dim3((unsigned)(k.MT * k.NT)),
+  hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>), dim3((unsigned)(k.MT * k.NT * k.S)),
                      dim3(kGemmThreads), lds, (hipStream_t)stream, k);
   return hipGetLastError();
 }
 
 }  // namespace
 
-TiledShape tiled_shape(int64_t M, int64_t N) {
-  // 256-row tiles; 224 columns when that gives whole waves of 256 tiles.
+TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_base) {
+  // Large M: 256-row tiles (224 columns when that gives whole waves of 256
+  // tiles), no split.  Mid-size M, where those tiles would not fill the GPU:
+  // 128 x 128 tiles (M > 128) or 64 x 128 tiles, with K split so that about
+  // one workgroup per CU runs, each split at least four 128-k chunks.
   TiledShape t;
-  const int64_t nblk = n_pad(N) / 16;
+  const int64_t nblk = n_pad(N) / 16, KC = k_pad(K) / kKChunk;
   t.tm = 256;
   t.tn = (nblk % 14 == 0 && nblk >= 14) ? 224 : 256;
-  t.grid = (int)(ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16));
+  int64_t tiles = ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16);
+  if (tiles < (int64_t)cus * 3 / 4) {
+    t.tm = M > 128 ? 128 : 64;
+    t.tn = 128;
+    tiles = ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16);
+    int64_t S = cus / tiles;
+    const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(KC / 4, t.tm == 64 ? 16 : 8));
+    S = std::max<int64_t>(1, std::min(S, max_s));
+    t.cps = (int)ceil_div(KC, S);
+    t.split = (int)ceil_div(KC, t.cps);
+  } else {
+    t.split = 1;
+    t.cps = (int)KC;
+  }
+  t.mt = (int)ceil_div(M, t.tm);
+  t.nt = (int)ceil_div(nblk, t.tn / 16);
+  t.grid = t.mt * t.nt * t.split;
+  if (t.split > 1) {
+    t.ws_part = (size_t)round_up((int64_t)scratch_base, 256);
+    t.ws_bytes = t.ws_part + (size_t)t.mt * t.nt * t.split * t.tm * t.tn * 4;
+    t.fits = (int64_t)t.mt * t.nt <= kMaxSyncWords - 128;
+  }
   return t;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream) {
+  const TiledShape t = tiled_shape(a.M, a.K, a.N, plan.cus, a.scratch_base);
   GemmKArgs k;
   k.X = (const half_t*)a.X;
   k.Wq = (const u32x4_t*)a.Wq;
@@ -273,9 +351,16 @@ hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream
   k.NBLK = (int)(n_pad(a.N) / kNBlock);
   k.ps = a.ec ? (int)p_stride(a.rank) : 0;
   k.ec = a.ec;
-  k.MT = k.NT = 0;
-  if (plan.tile_n == 224) return launch_cfg<8, 7, 2, 2>(k, stream);
-  return launch_cfg<8, 8, 2, 2>(k, stream);
+  k.MT = t.mt; k.NT = t.nt;
+  k.S = t.split; k.CPS = t.cps;
+  k.part = t.split > 1 ? (float*)((char*)a.workspace + t.ws_part) : nullptr;
+  k.tickets = t.split > 1 ? (uint32_t*)((char*)a.workspace + kGemmSyncOffset) + 128 : nullptr;
+  // 256-row tiles never split; the mid-size tiles are built with the split
+  // path, which they skip when S is 1.
+  if (t.tm == 256 && t.tn == 224) return launch_cfg<8, 7, 2, 2, false>(k, stream);
+  if (t.tm == 256) return launch_cfg<8, 8, 2, 2, false>(k, stream);
+  if (t.tm == 128) return launch_cfg<4, 4, 2, 2, true>(k, stream);
+  return launch_cfg<2, 4, 2, 2, true>(k, stream);
 }
 
 }  // namespace spear

@@ -86,6 +86,8 @@ struct GemmArgs {
   void* Y;             // fp16 [M, N]
   int32_t M, K, N, rank;
   int32_t ec;          // apply the gated EC term
+  void* workspace;     // base (split partials and tile counters), may be null without splits
+  size_t scratch_base; // first workspace byte the GEMM may use as scratch
 };
 
 // Skinny (M <= 16) kernel: tile shape, producers and workspace layout.
@@ -127,9 +129,17 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream);
 
 // Tiled (M > 16) kernel: tile shape and grid.
 struct TiledShape {
-  int tm = 256, tn = 256, grid = 0;
+  int tm = 256, tn = 256;   // tile rows and columns
+  int mt = 0, nt = 0;       // row and column tiles
+  int split = 1;            // K splits (partial sums added by the last to arrive)
+  int cps = 0;              // 128-k chunks per split
+  int grid = 0;
+  size_t ws_part = 0;       // split partials (bytes from the workspace base)
+  size_t ws_bytes = 0;      // workspace this kernel needs (0: none)
+  bool fits = true;         // tile counters fit the counter header
 };
-TiledShape tiled_shape(int64_t M, int64_t N);
+// scratch_base: first byte of the workspace this kernel may use as scratch.
+TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_base);
 
 hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);

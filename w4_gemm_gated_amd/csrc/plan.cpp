@@ -10,7 +10,8 @@
 //     launch, then the tiled GEMM with the gated epilogue);
 //   * the per-token gate-value decision (skip the EC term where every gate of
 //     a wave's rows is below tau) is taken on the device in the epilogue.
-//   * main kernel family by M: skinny (M <= 16 rows) or tiled (256-row tiles).
+//   * main kernel family by M: skinny (M <= 16 rows) or tiled (256-row tiles;
+//     128- or 64-row tiles with K split where those would not fill the GPU).
 #include <cmath>
 #include <cstring>
 
@@ -82,11 +83,13 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     // X and the packed weight are addressed with 32-bit buffer offsets.
     if ((int64_t)d.M * d.K * 2 > INT32_MAX || n_pad(d.N) * k_pad(d.K) / 2 > INT32_MAX)
       return SPEAR_ERR_UNSUPPORTED;
-    const TiledShape t = tiled_shape(d.M, d.N);
+    const TiledShape t = tiled_shape(d.M, d.K, d.N, cus, scratch_base);
+    if (!t.fits) return SPEAR_ERR_UNSUPPORTED;
     p.kernel = 1;
     p.tile_m = t.tm; p.tile_n = t.tn;
-    p.split_k = 1;
+    p.split_k = t.split;
     p.grid = t.grid;
+    if (t.ws_bytes > ws) ws = t.ws_bytes;
   }
   p.workspace_bytes = d.M > 0 ? ws : 0;
   *plan = p;
