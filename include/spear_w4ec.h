@@ -3,11 +3,11 @@
  * per-token-gated low-rank Error Compensator (EC).
  *
  * Method: "SPEAR: A System for Post-Quantization Error-Adaptive Recovery
- * Enabling Efficient Low-Bit LLM Serving" (arXiv 2606.11244), Abstract:
- * 4-bit per-channel weights, lightweight Error Compensators modulated by
- * per-token gates, the post-EC computation fused into the low-bit GEMM, and an
- * adaptive kernel-fusion dispatch.  The abstract gives no formulas; this
- * library computes
+ * Enabling Efficient Low-Bit LLM Serving" (arXiv 2606.11244), abstract: weights
+ * in 4 bits with one scale per output channel, small error-compensating
+ * branches whose output each token's gate scales, the second half of that
+ * branch computed inside the low-bit GEMM, and a per-call choice of how much
+ * to fuse.  The page gives no formulas; this library computes
  *
  *     Y = X . dequant(Wq, s) + g' (.) ((X . A) . B)
  *     g = sigmoid(X . w_g + b_g),  g' = g, or g . [g >= tau] when tau > 0
@@ -53,7 +53,7 @@ typedef enum spear_status {
   SPEAR_ERR_INVALID_ARGUMENT = 8     /* a non-finite bias/threshold or an unknown variant */
 } spear_status_t;
 
-/* Kernel-fusion variants (abstract: "adaptive kernel-fusion dispatch"). */
+/* Kernel-fusion variants (SPEAR page, abstract: the fusion is chosen per call). */
 typedef enum spear_variant {
   SPEAR_VARIANT_AUTO = 0,  /* let spear_dispatch_plan choose */
   SPEAR_VARIANT_FUSED = 1, /* one launch: EC projection and gate, W4 GEMM, gated EC epilogue */
@@ -103,7 +103,8 @@ uint32_t spear_abi_version(void);
 spear_status_t spear_packed_bytes(int32_t K, int32_t N, size_t* bytes);
 
 /*
- * spear_pack_w4 -- quantize and pack a weight (abstract: W4 per-channel).
+ * spear_pack_w4 -- quantize and pack a weight (SPEAR page, abstract: 4-bit weights,
+ * one scale per output channel).
  *   W      fp16 [K, N] row-major (input dimension first; an nn.Linear weight
  *          is W = weight^T), 2-byte aligned.
  *   Wq     output, spear_packed_bytes(K, N) bytes, 16-byte aligned.
@@ -122,7 +123,7 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
 
 /*
  * spear_dispatch_plan -- choose the kernel-fusion variant and the launch
- * shape for a call (abstract: "adaptive kernel-fusion dispatch").
+ * shape for a call (SPEAR page, abstract: the fusion variant adapts to the call).
  * Host only; touches the device only to read its CU count when
  * desc->device_cus == 0 (cached per device).
  * Rules: rank 0 or variant NO_EC -> NO_EC; AUTO -> FUSED when M is at most

@@ -8,10 +8,10 @@ and its Python binding never import it, and it imports nothing from them.
 
 Source of the method: "SPEAR: A System for Post-Quantization Error-Adaptive
 Recovery Enabling Efficient Low-Bit LLM Serving" (arXiv 2606.11244),
-Abstract.  The abstract names per-channel W4 weight quantization, lightweight
-Error Compensators (ECs) modulated by per-token gates, and the fusion of the
-post-EC computation into the low-bit GEMM.  It gives no formulas; the layer
-computed here is
+abstract.  The page describes 4-bit weights with one scale per output channel,
+small error-compensating branches (ECs) whose output a per-token gate scales,
+and the second half of that branch computed inside the low-bit GEMM.  It gives
+no formulas; the layer computed here is
 
     Y = X . dequant(Wq, s) + g (.) ((X . A) . B),   g = sigmoid(X . w_g + b_g)
 

@@ -20,7 +20,7 @@ import numpy as np
 LAYOUT_ID = 2
 K_CHUNK = 128   # k extent of one 1 KiB tile
 N_BLOCK = 16    # column extent of one panel
-_QMAX = 7       # symmetric int4: codes -7..7 (abstract: "W4", per-channel)
+_QMAX = 7       # symmetric int4: codes -7..7 (SPEAR page, abstract: 4-bit, per channel)
 
 
 def padded_dims(K, N):

@@ -1,8 +1,8 @@
 """Pins of the oracle's gate and layer output (CPU only).
 
 Layer: Y = X . dequant(Wq, s) + g (.) ((X . A) . B), g = sigmoid(X . w_g + b_g)
-(SPEAR abstract: ECs "modulated by per-token gates", post-EC computation fused
-into the low-bit GEMM).  Every pin below comes from outside the oracle: a
+(SPEAR page, abstract: error compensators scaled per token by a gate, their
+second half computed inside the low-bit GEMM).  Every pin below comes from outside the oracle: a
 closed form, a special case that reduces to a textbook product, a library
 routine, brute force, or an exactly rounded sum.
 """

@@ -1,7 +1,8 @@
 """Pins of the oracle's quantizer and bit packing (CPU only).
 
-The quantizer follows the SPEAR abstract's "per-channel" W4 setting with the
-symmetric reading s = fp16(max|w| / 7), q = clamp(rint(w / s), -7, 7).
+The quantizer follows the SPEAR page's 4-bit, one-scale-per-output-channel
+setting (abstract) with the symmetric reading s = fp16(max|w| / 7),
+q = clamp(rint(w / s), -7, 7).
 """
 import json
 import os

@@ -1,5 +1,5 @@
-// EC projection and per-token gate in one pass over X (SPEAR abstract:
-// "lightweight Error Compensators (ECs) modulated by per-token gates"):
+// EC projection and per-token gate in one pass over X (SPEAR page, abstract:
+// the small error compensators are scaled per token by a gate):
 //
 //   [P | z] = X . [A | w_g]      (fp32 accumulation on the matrix cores)
 //   g'      = sigmoid(z + b_g), set to 0 when tau > 0 and g < tau

@@ -1,5 +1,6 @@
 // Tiled (prefill, M > 16) W4 GEMM with the gated EC term in its epilogue
-// (SPEAR abstract: "fuse the post-EC computation into low-bit GEMMs"):
+// (SPEAR page, abstract: the work after the EC projection runs inside the
+// low-bit GEMM):
 //
 //   acc[m, n] = sum_k X[m, k] q[k, n]                  (fp16 x fp16 -> fp32 MFMA)
 //   Y[m, n]   = fp16( s[n] acc[m, n] + sum_j (g'[m] P[m, j]) B[j, n] )

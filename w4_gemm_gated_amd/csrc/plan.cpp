@@ -1,4 +1,4 @@
-// Host planner: the adaptive kernel-fusion dispatch of the SPEAR abstract,
+// Host planner: the per-call choice of fusion variant (SPEAR page, abstract),
 // reduced to what one GPU needs.  Pure host arithmetic on the descriptor; the
 // device is touched only by the caller (api.cpp) to read the CU count.
 //

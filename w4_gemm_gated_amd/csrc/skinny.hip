@@ -1,7 +1,7 @@
 // Skinny (decode, M <= 16 rows) W4 GEMM with the gated EC fused in: one launch
 // computes the EC projection and gate, the W4 product and the gated EC
-// epilogue (SPEAR abstract: ECs modulated by per-token gates, the post-EC
-// computation fused into the low-bit GEMM).
+// epilogue (SPEAR page, abstract: per-token gated error compensators, their
+// second half computed inside the low-bit GEMM).
 //
 // At decode the layer is bound by reading the packed weight (K N / 2 bytes)
 // from HBM, so the kernel puts the whole weight in flight at once:
