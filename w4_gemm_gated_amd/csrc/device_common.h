@@ -121,5 +121,16 @@ __device__ __forceinline__ uint32_t add_dev_u32(uint32_t* p, uint32_t v) {
 }
 // Wait until every memory instruction this wave issued has completed.
 __device__ __forceinline__ void drain_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same wait in a form the compiler sees (s_waitcnt with vmcnt = 0 and
+// the other counters at their maximum, gfx9 encoding).  A wait written in
+// inline asm is opaque to the compiler's own wait insertion, which then adds
+// a second vmcnt(0) at the first use of a loaded register, possibly after
+// loads issued meanwhile; this form lets it know those registers are ready.
+// The empty asm statements keep memory accesses from moving across it.
+__device__ __forceinline__ void wait_vm_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace spear

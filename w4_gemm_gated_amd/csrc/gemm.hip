@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
   load_w(kc_begin, wcur);
   for (int kc = kc_begin; kc < kc_end; ++kc) {
     const int st = (kc - kc_begin) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_all();
     __syncthreads();
     if (kc + 1 < kc_end) {
       issue_x(kc + 1, st ^ 1);
@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[e] = (half_t)(gv * pv[e]);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_all();
     __syncthreads();
     if (any_gate) {
       const int jbn = min(kEcChunk, jblocks * 32 - j0) / 32;

@@ -17,13 +17,12 @@
 //     each compute [P | z] = X [A | w_g] over one K slab for the M rows and
 //     publish it in the hand-off table, each value tagged with the call's
 //     epoch;
-//   * every GEMM workgroup requests the hand-off table right behind its
-//     weight loads.  A CU serves its memory requests in order, so the table
-//     arrives when the workgroup's weight stream has, by which time the
-//     producers (on CUs with no weight stream, and a head start) have
-//     normally published it; the tags tell whether they had, and a bounded
-//     wait covers the entries they had not.  The workgroup adds the slabs in
-//     fixed order and applies the gate itself.
+//   * every GEMM workgroup requests the hand-off table once its matrix
+//     instructions are done, by which time the producers (on CUs with no
+//     weight stream, and a head start) have normally published it; the tags
+//     tell whether they had, and a bounded wait covers the entries they had
+//     not.  The workgroup adds the slabs in fixed order and applies the gate
+//     itself.
 // Data crosses workgroups only through device-coherent stores and loads (see
 // device_common.h), never through L2 write-backs.  Every call returns its
 // counters to zero and advances the epoch; the last GEMM workgroup to finish
@@ -254,25 +253,22 @@ constexpr size_t static_lds_bytes(int nbw) { return (size_t)3 * kWave * nbw * 16
 // g'); then the fused variant's copy of the hand-off slabs Ht[P][M][r1p] or
 // the split variant's Pt[16][ps] floats and gt[16].
 //
-// The EC operands are loaded into registers, a fixed number per thread, with
-// straight-line code: the B tile and the split variant's P and g ahead of the
-// weight stream (they are ready), the hand-off slabs right behind it.  (With
-// a loop, or with a direct-to-LDS copy, among these loads the compiler can no
-// longer count the loads in flight, and it waits for all of them before the
-// first matrix instruction.)  Whatever these do not cover is loaded after the
-// matrix instructions.
+// The EC operands that are ready at the start (the B tile, the split
+// variant's P and g) are loaded into registers ahead of the weight stream, a
+// fixed number per thread, with straight-line code.  (With a loop, or with a
+// direct-to-LDS copy, among these loads the compiler can no longer count the
+// loads in flight, and it waits for all of them before the first matrix
+// instruction.)  Whatever these do not cover, and the fused variant's
+// hand-off slabs, are loaded after the matrix instructions.
 constexpr int kBLoads = 4;    // B tile halves per thread
 constexpr int kPLoads = 1;    // split: 16-byte units of P per thread
-constexpr int kHLoads = 4;    // fused: 16-byte hand-off units (two entries) per thread
-constexpr int kHCovered = kHLoads * kThreads;   // 16-byte units loaded ahead
 __host__ __device__ __forceinline__ size_t gemm_bs_bytes(int ps, int tn) {
   return ((size_t)ps * tn * 2 + 15) & ~(size_t)15;
 }
 __host__ __device__ __forceinline__ size_t gemm_pc_bytes(int rank) { return ((size_t)16 * (rank + 1) * 4 + 15) & ~(size_t)15; }
 __host__ __device__ __forceinline__ size_t gemm_table_bytes(int ec_mode, int ps, int r1p, int P, int M) {
   if (ec_mode == 1) {
-    const size_t need = (size_t)P * M * r1p * 8, ahead = (size_t)kHCovered * 16;
-    return need > ahead ? need : ahead;
+    return (size_t)P * M * r1p * 8;
   }
   return (size_t)16 * ps * 4 + 16 * 4;
 }
@@ -373,20 +369,7 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
       for (int j = 0; j < 4; ++j) xa[c][j] = zero_half8();
     }
   }
-  // ---- fused: the hand-off slabs behind the weight stream (device-coherent
-  // loads; units past the table read as zeros, tag 0).
   const int handoff_units = ECM == 1 ? a.P * a.M * a.r1p / 2 : 0;   // 16-byte units, two entries each
-  u32x4_t hreg[kHLoads];
-  if (ECM == 1) {
-    const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.handoff, (uint32_t)((size_t)handoff_units * 16));
-#pragma unroll
-    for (int i = 0; i < kHLoads; ++i) {
-      const int u = i * kThreads + tid;
-      hreg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                hr, u < handoff_units ? (uint32_t)u * 16u : kOutOfRange, 0,
-                                                kCachePolicySc1));
-    }
-  }
   // Keep every load above this point (no load may sink into the
   // matrix-instruction block and pay a second round trip).
   __builtin_amdgcn_sched_barrier(0);
@@ -412,13 +395,6 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
     for (int q = kBLoads * kThreads + tid; q < brows * TN; q += kThreads) {
       const int row = min(q / TN, a.rank - 1), col = min(n0 + q % TN, a.N - 1);
       Bs[q] = a.Bec[(size_t)row * a.N + col];
-    }
-  }
-  if (ECM == 1) {
-#pragma unroll
-    for (int i = 0; i < kHLoads; ++i) {
-      const int u = i * kThreads + tid;
-      if (u < handoff_units) reinterpret_cast<u32x4_t*>(table)[u] = hreg[i];
     }
   }
   if (ECM == 2) {
@@ -498,18 +474,21 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
       const bool ok1 = (e0 + 1) % a.r1p >= r1 || v[3] == tag;
       return ok0 && ok1;
     };
-    // Units past the registers' reach: one batch of loads now.
-    for (int u0 = kHCovered; u0 < handoff_units; u0 += 8 * kThreads) {
-      u32x4_t v[8];
+    // The whole table, after the matrix instructions: batches of sixteen
+    // loads per thread.  (Requested any earlier, the loads would queue
+    // behind the weight stream and be served about when it is, normally just
+    // before the producers publish, which costs a second round trip.)
+    for (int u0 = 0; u0 < handoff_units; u0 += 16 * kThreads) {
+      u32x4_t v[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 16; ++i) {
         const int u = u0 + i * kThreads + tid;
         v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                hr, u < handoff_units ? (uint32_t)u * 16u : kOutOfRange, 0,
                                                kCachePolicySc1));
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 16; ++i) {
         const int u = u0 + i * kThreads + tid;
         if (u < handoff_units) Hu[u] = v[i];
       }
