@@ -67,8 +67,17 @@ def plan(lib, M, K, N, r, variant=0, cus=256, bias=0.0, tau=0.0):
 def test_dispatch_rules(lib):
     st, p = plan(lib, 16, 4096, 4096, 32)
     assert st == 0 and p.variant in (1, 2) and p.kernel == 0 and p.workspace_bytes > 0
+    # tiled fused: 32 row tiles x 8 K slices of EC workgroups lead the grid,
+    # then the 8 x 64 tiles of 256 x 224
     st, p = plan(lib, 2048, 4096, 14336, 64)
-    assert st == 0 and p.variant == 2 and p.kernel == 1 and p.workspace_bytes > 0
+    assert st == 0 and p.variant == 1 and p.kernel == 1 and p.workspace_bytes > 0
+    assert p.producers == 32 * 8 and p.grid == 256 + 8 * 64 and p.tile_m == 256 and p.tile_n == 224
+    st, p = plan(lib, 2048, 4096, 14336, 64, variant=2)
+    assert st == 0 and p.variant == 2 and p.kernel == 1 and p.grid == 8 * 64
+    # EC workgroups are padded to a multiple of 8 (the GEMM tiles keep their
+    # XCD order): 1 row tile x 14 K slices -> 16
+    st, p = plan(lib, 64, 14336, 4096, 64)
+    assert st == 0 and p.variant == 1 and p.producers == 14 and p.grid == 16 + 32 * p.split_k
     st, p = plan(lib, 16, 4096, 4096, 32)
     # fused: the EC producer workgroups, then the GEMM tiles (256 panels of
     # 16 columns, one K range)
@@ -83,8 +92,10 @@ def test_dispatch_rules(lib):
     assert st == 0 and p.variant == 3 and p.producers == 0
     st, p = plan(lib, 16, 4096, 4096, 32, variant=2)
     assert st == 0 and p.variant == 2
-    st, p = plan(lib, 64, 4096, 4096, 32, variant=1)
-    assert st == 3                        # the fused variant is built for M <= 16
+    st, p = plan(lib, 64, 4096, 4096, 30, variant=1)
+    assert st == 3                        # fused (skinny or tiled) needs rank % 4 == 0
+    st, p = plan(lib, 64, 4096, 4096, 30)
+    assert st == 0 and p.variant == 2
     st, p = plan(lib, 2048, 4096, 14336, 32, variant=3)
     assert st == 0 and p.variant == 3 and p.split_k == 1 and p.workspace_bytes == 0
     # mid-size M: 64-row tiles with K split over workgroups (partials in the workspace)

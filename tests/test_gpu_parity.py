@@ -144,20 +144,22 @@ def test_decode_workload(M):
     layer_case(w["X"][:M], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][M], 0.0, "auto", f"decode M={M}")
 
 
-def test_prefill_workload_sampled_rows():
+@pytest.mark.parametrize("variant", ["auto", "split"])
+def test_prefill_workload_sampled_rows(variant):
     w = workloads.workload(3)
     rows = np.sort(np.random.default_rng(3).choice(2048, 48, replace=False))
     rows = np.concatenate([[0, 1, 2047], rows])
-    layer_case(w["X"], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][2048], 0.0, "auto",
-               "prefill M=2048 (51 sampled rows)", rows=rows)
+    layer_case(w["X"], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][2048], 0.0, variant,
+               f"prefill M=2048 {variant} (51 sampled rows)", rows=rows)
 
 
+@pytest.mark.parametrize("variant", ["fused", "split"])
 @pytest.mark.parametrize("M,tau", [(64, 0.0), (64, 0.05), (512, 0.0), (512, 0.05)])
-def test_mixed_gate_workload(M, tau):
+def test_mixed_gate_workload(M, tau, variant):
     w = workloads.workload(4)
     rows = None if M == 64 else np.sort(np.random.default_rng(4).choice(M, 96, replace=False))
-    layer_case(w["X"][:M], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][M], tau, "auto",
-               f"mixed-gate M={M} tau={tau}", rows=rows)
+    layer_case(w["X"][:M], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][M], tau, variant,
+               f"mixed-gate M={M} tau={tau} {variant}", rows=rows)
 
 
 @pytest.mark.parametrize("layer", range(7))
@@ -182,6 +184,18 @@ def test_fused_ragged_shapes(M, K, N, r):
     blocks of A (rank % 16 != 0), one-column outputs and the largest rank."""
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=3 * M + K + N + r, outliers=True)
     layer_case(X, W, A, B, w_g, -0.5, 0.0, "fused", f"fused ragged M={M} K={K} N={N} r={r}")
+
+
+@pytest.mark.parametrize("variant", ["fused", "split"])
+@pytest.mark.parametrize("M,K,N,r", [(17, 264, 40, 4), (33, 512, 48, 256), (130, 392, 200, 32),
+                                     (300, 1000, 100, 20), (520, 2056, 300, 36), (100, 1024, 64, 64)])
+def test_tiled_ragged_shapes(M, K, N, r, variant):
+    """The tiled path (M > 16) in both EC variants on K tails, partial row and
+    column tiles, partial column blocks of A and the largest rank; the fused
+    launch's EC workgroups publish P and g' for the GEMM tiles of the same
+    launch."""
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=5 * M + K + N + r, outliers=True)
+    layer_case(X, W, A, B, w_g, -0.5, 0.0, variant, f"tiled {variant} M={M} K={K} N={N} r={r}")
 
 
 def test_empty_batch():
@@ -230,6 +244,34 @@ def test_repeat_calls_deterministic_and_workspace_clean():
     assert int(counters[epoch_word].item()) == 2
     counters[epoch_word] = 0
     assert int(counters.abs().sum().item()) == 0
+
+
+def test_tiled_fused_repeat_calls_and_workspace():
+    """Two fused tiled calls on one workspace: identical results; the counters
+    are back at zero, the epoch counts the calls and the ready flags of the
+    EC row tiles (words 4096.. of the EC counter region) hold the last call's
+    tag."""
+    M, K, N, r = 130, 392, 200, 32
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=11, outliers=True)
+    Wq_d, s_d = sp.spear_pack_w4(cuda(W))
+    p = sp.spear_dispatch_plan(M, K, N, r, 0.3, variant="fused")
+    assert p.variant == 1 and p.kernel == 1
+    ws = torch.zeros(p.workspace_bytes, dtype=torch.uint8, device=DEV)
+    args = (cuda(X), Wq_d, s_d, cuda(A), cuda(B), cuda(w_g), 0.3)
+    Y1 = sp.spear_w4ec_linear(*args, variant="fused", N=N, plan=p, workspace=ws).clone()
+    Y2 = sp.spear_w4ec_linear(*args, variant="fused", N=N, plan=p, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    words = ws[: 64 * 1024].view(torch.int32).clone()
+    epoch_word = 32 * 1024 // 4 + 96
+    m_tiles = (M + 63) // 64
+    assert int(words[epoch_word].item()) == 2
+    assert [int(v) for v in words[4096:4096 + m_tiles].tolist()] == [2] * m_tiles
+    words[epoch_word] = 0
+    words[4096:4096 + m_tiles] = 0
+    assert int(words.abs().sum().item()) == 0
+    Wq_o, s_o = oracle.pack_w4(W)
+    compare(Y1.cpu().numpy(), X, Wq_o, s_o, A, B, w_g, 0.3, 0.0, K, N, "tiled fused repeat")
 
 
 @pytest.mark.parametrize("variant", ["fused", "split", "no_ec"])

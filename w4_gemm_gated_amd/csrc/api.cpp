@@ -169,17 +169,21 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
   if (p.variant == SPEAR_VARIANT_FUSED && (!aligned(A, 16) || !aligned(w_g, 16))) return SPEAR_ERR_MISALIGNED;
 
   const bool skinny = p.kernel == 0;
+  const bool fused_tiled = p.variant == SPEAR_VARIANT_FUSED && !skinny;
   size_t ec_bytes = 0;
   EcWorkspace L;
-  if (p.variant == SPEAR_VARIANT_SPLIT) {
+  EcArgs e;
+  std::memset(&e, 0, sizeof(e));
+  if (p.variant == SPEAR_VARIANT_SPLIT || fused_tiled) {
     L = ec_workspace_layout(desc->M, desc->K, desc->rank);
     ec_bytes = L.bytes;
-    EcArgs e;
     e.X = X; e.A = A; e.w_g = w_g;
     e.M = desc->M; e.K = desc->K; e.rank = desc->rank;
     e.gate_bias = desc->gate_bias; e.skip_tau = desc->skip_tau;
     e.workspace = workspace;
     e.P_out = nullptr; e.g_out = nullptr; e.p_out_stride = 0;
+  }
+  if (p.variant == SPEAR_VARIANT_SPLIT) {
     st = hip_status(launch_ec_project(e, stream));
     if (st != SPEAR_OK) return st;
   }
@@ -208,6 +212,8 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
     ga.g = (const float*)((const char*)workspace + L.g);
     ga.ec = 1;
   }
+  ga.fused = fused_tiled ? 1 : 0;
+  ga.ecargs = e;
   return hip_status(launch_gemm(ga, p, stream));
 }
 

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "ec_block.h"
 #include "internal.h"
 
 namespace spear {
@@ -55,6 +56,20 @@ struct GemmKArgs {
   int S, CPS;             // K splits, 128-k chunks per split
   float* part;            // [tile][S][MBW * NBW][256 threads] float4 partials
   uint32_t* tickets;      // [tile] split counters (back to zero after each call)
+  // Fused launch only: P and g are produced by the launch's EC workgroups.
+  const uint32_t* ready;  // [ec row tiles of 64] flags, raised to the call's tag
+  int ec_tiles;           // EC row tiles
+  uint32_t* error;        // set when a wait for a ready flag gives up
+  uint32_t spin_limit;
+};
+
+// The fused launch: E EC workgroups (the first blocks), then the GEMM tiles.
+struct FusedKArgs {
+  GemmKArgs g;
+  EcKArgs e;
+  int E;                  // leading blocks that are EC workgroups (a multiple of 8)
+  int ec_blocks;          // of which the real ones (m_tiles x splits)
+  uint32_t* sync;         // GEMM sync words (finishers, epoch)
 };
 
 __device__ __forceinline__ void copy16_to_lds(const void* src, void* dst_wave_base) {
@@ -64,16 +79,18 @@ __device__ __forceinline__ void copy2_to_lds(const void* src, void* dst_wave_bas
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 2, 0, 0);
 }
 
-// Wave tile MBW x NBW blocks of 16 x 16; workgroup WM x WN waves.  SPLIT:
-// K split over a.S workgroups per tile.
-template <int MBW, int NBW, int WM, int WN, bool SPLIT>
-__global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a) {
+// One GEMM workgroup (tile block `block`).  Wave tile MBW x NBW blocks of
+// 16 x 16; workgroup WM x WN waves.  SPLIT: K split over a.S workgroups per
+// tile.  FUSED: P and g come from EC workgroups of the same launch; the
+// epilogue waits for their ready flags (raised to `tag`) and reads P and g
+// with device-coherent loads.
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool FUSED>
+__device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsigned char* lds, uint32_t tag) {
   static_assert(WM * WN * kWave == kGemmThreads, "four waves");
   constexpr int TM = 16 * MBW * WM;
   constexpr int TN = 16 * NBW * WN;
   constexpr int kStageHalves = TM * kKt;                    // one X stage
   constexpr int kCopiesPerWave = TM * kUnitsPerRow / kWave / 4;
-  extern __shared__ __align__(16) unsigned char lds[];
   half_t* xs = reinterpret_cast<half_t*>(lds);                // [2][TM][kKt], swizzled units
 
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -85,9 +102,9 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
   // tiles x, x + 8, ... and walks the column tiles of each.
   int m_tile, n_tile;
   const int tiles = a.MT * a.NT;
-  const int split = blockIdx.x / tiles;
+  const int split = block / tiles;
   {
-    const int bid = blockIdx.x % tiles;
+    const int bid = block % tiles;
     if (a.MT % 8 == 0) {
       const int xcd = bid % 8, j = bid / 8;
       m_tile = xcd + 8 * (j / a.NT);
@@ -208,7 +225,7 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
   // is done with the X stages) holds the B rows bs[64][TN] (dword slots, fp16
   // in the low half; rows >= rank clamped: they meet zero P columns) and
   // pg[TM][64] = fp16(g' P) of the tile's rows (rows >= M clamped: never
-  // stored).
+  // stored), after gs[TM], the tile's gates.
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     const float s = (float)a.scales[min((nb_base + nb) * 16 + c16, a.N - 1)];
@@ -216,15 +233,37 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
     for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] *= s;
   }
   const int jblocks = a.ec ? a.ps / 32 : 0;
-  bool any_gate = false;
-#pragma unroll
-  for (int mb = 0; mb < MBW; ++mb) {
-    const int row = m0 + wm * MBW * 16 + mb * 16 + c16;
-    any_gate |= jblocks > 0 && row < a.M && a.g[min(row, a.M - 1)] != 0.0f;
-  }
-  any_gate = __any(any_gate);
   uint32_t* bs = reinterpret_cast<uint32_t*>(lds);
   half_t* pg = reinterpret_cast<half_t*>(lds + (size_t)kEcChunk * TN * 4);
+  float* gs = reinterpret_cast<float*>(lds + (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2);
+  bool any_gate = false;
+  if (jblocks > 0) {
+    if (FUSED && tid == 0) {
+      // Wait until the EC row tiles under this tile's rows are published.
+      const int t_end = min(a.ec_tiles, (m0 + TM + 63) / 64);
+      for (int t = m0 / 64; t < t_end; ++t) {
+        uint32_t n = 0;
+        while (ld_dev_u32(&a.ready[t]) != tag) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++n > a.spin_limit) {
+            st_dev_u32(a.error, 1u);
+            break;
+          }
+        }
+      }
+    }
+    __syncthreads();                           // also: every wave is done with the X stages
+    // gs[TM] = g' of the tile's rows (0 past M), one load per thread.
+    if (tid < TM) gs[tid] = m0 + tid < a.M ? (FUSED ? ld_dev(&a.g[m0 + tid]) : a.g[m0 + tid]) : 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) any_gate |= gs[wm * MBW * 16 + mb * 16 + c16] != 0.0f;
+    any_gate = __any(any_gate);
+  }
+  // P through a buffer resource (columns >= ps read as zeros): device-coherent
+  // loads when the same launch produced it.
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((size_t)a.M * a.ps * 4));
+  constexpr int kPUnits = TM * (kEcChunk / 4) / kGemmThreads;   // 16-byte P units per thread per chunk
   const int n0 = n_tile * TN;
   for (int j0 = 0; j0 < jblocks * 32; j0 += kEcChunk) {
     __syncthreads();
@@ -232,16 +271,24 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
       const int idx = e + lane, r = idx / TN, c = idx % TN;
       copy2_to_lds(a.B + (size_t)min(j0 + r, a.rank - 1) * a.N + min(n0 + c, a.N - 1), bs + e);
     }
-    for (int idx = tid; idx < TM * (kEcChunk / 4); idx += kGemmThreads) {
-      const int r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
-      const int row = min(m0 + r, a.M - 1);
-      const int col = j0 + c4 * 4;
-      const float gv = a.g[row];
-      float4_t pv = zero_float4();
-      if (col < a.ps) pv = *reinterpret_cast<const float4_t*>(a.P + (size_t)row * a.ps + col);
+    // pg[TM][64] = fp16(g' P): every P load of the chunk is issued before the
+    // first is used (one memory round trip).
+    float4_t pv[kPUnits];
+#pragma unroll
+    for (int i = 0; i < kPUnits; ++i) {
+      const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
+      const int row = min(m0 + r, a.M - 1), col = j0 + c4 * 4;
+      const uint32_t off = col < a.ps ? (uint32_t)(((size_t)row * a.ps + col) * 4) : kOutOfRange;
+      pv[i] = FUSED ? buffer_load_f4_dev(pr, off)
+                    : __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < kPUnits; ++i) {
+      const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
+      const float gv = gs[r];
       half_t* dst = pg + (size_t)r * kEcChunk + c4 * 4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = (half_t)(gv * pv[e]);
+      for (int e = 0; e < 4; ++e) dst[e] = (half_t)(gv * pv[i][e]);
     }
     wait_vm_all();
     __syncthreads();
@@ -285,8 +332,42 @@ template <int MBW, int NBW, int WM, int WN>
 constexpr size_t tile_lds_bytes() {
   constexpr int TM = 16 * MBW * WM, TN = 16 * NBW * WN;
   constexpr size_t stages = (size_t)2 * TM * kKt * 2;
-  constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2;
+  constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
   return stages > epilogue ? stages : epilogue;
+}
+
+template <int MBW, int NBW, int WM, int WN, bool SPLIT>
+__global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  gemm_block<MBW, NBW, WM, WN, SPLIT, false>(a, blockIdx.x, lds, 0u);
+}
+
+// Fused tiled launch: blocks [0, E) are EC workgroups (the first ec_blocks
+// of them real, the rest padding so that the GEMM blocks keep their XCD
+// order), the others GEMM tiles.  EC workgroups have the lowest block
+// indices, so they are dispatched before any GEMM workgroup and never wait
+// for one; a GEMM workgroup waits only in its epilogue, for ready flags that
+// the EC workgroups raise.  Every block reads the call epoch first and counts
+// itself out last; the last to finish returns the finisher count to zero and
+// advances the epoch (every block has read it by then).
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB>
+__global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs f) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const uint32_t tag = ld_dev_u32(&f.sync[kSyncEpoch]) + 1u;
+  const int b = blockIdx.x;
+  if (b < f.E) {
+    if (b < f.ec_blocks) ec_block<true, true, PB>(f.e, lds, b % f.e.m_tiles, b / f.e.m_tiles, tag);
+  } else {
+    gemm_block<MBW, NBW, WM, WN, SPLIT, true>(f.g, b - f.E, lds, tag);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t before = add_dev_u32(&f.sync[kSyncFinishers], 1u);
+    if (before == gridDim.x - 1) {
+      st_dev_u32(&f.sync[kSyncFinishers], 0u);
+      st_dev_u32(&f.sync[kSyncEpoch], tag);
+    }
+  }
 }
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT>
@@ -299,6 +380,32 @@ hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
   hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>), dim3((unsigned)(k.MT * k.NT * k.S)),
                      dim3(kGemmThreads), lds, (hipStream_t)stream, k);
   return hipGetLastError();
+}
+
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB>
+hipError_t launch_fused_pb(const FusedKArgs& f, void* stream) {
+  const size_t tile = tile_lds_bytes<MBW, NBW, WM, WN>(), ec = ec_lds_bytes(f.e.ss, f.e.rp);
+  const size_t lds = tile > ec ? tile : ec;
+  if (ec_kb_for(PB) * 32 != f.e.ss || lds > kMaxLdsBytes - 1024) return hipErrorInvalidValue;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLdsBytes - 1024));
+  if (attr != hipSuccess) return attr;
+  const unsigned grid = (unsigned)(f.E + f.g.MT * f.g.NT * f.g.S);
+  hipLaunchKernelGGL((w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB>), dim3(grid), dim3(kGemmThreads), lds,
+                     (hipStream_t)stream, f);
+  return hipGetLastError();
+}
+
+template <int MBW, int NBW, int WM, int WN, bool SPLIT>
+hipError_t launch_fused(const FusedKArgs& f, void* stream) {
+  switch (ec_pb_for(f.e.rank)) {
+    case 1: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 1>(f, stream);
+    case 2: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 2>(f, stream);
+    case 4: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 4>(f, stream);
+    case 8: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 8>(f, stream);
+    default: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 16>(f, stream);
+  }
 }
 
 }  // namespace
@@ -355,7 +462,32 @@ hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream
   k.MT = t.mt; k.NT = t.nt;
   k.S = t.split; k.CPS = t.cps;
   k.part = t.split > 1 ? (float*)((char*)a.workspace + t.ws_part) : nullptr;
-  k.tickets = t.split > 1 ? (uint32_t*)((char*)a.workspace + kGemmSyncOffset) + 128 : nullptr;
+  uint32_t* sync = (uint32_t*)((char*)a.workspace + kGemmSyncOffset);
+  k.tickets = t.split > 1 ? sync + kSyncTiles : nullptr;
+  k.ready = nullptr;
+  k.ec_tiles = 0;
+  k.error = sync + kSyncError;
+  k.spin_limit = 1u << 20;   // ~0.5 s of polling: far beyond any healthy wait
+  if (a.fused) {
+    // EC workgroups first (P and g into the EC workspace, ready flags in the
+    // EC counter region), then the GEMM tiles.
+    const EcWorkspace L = ec_workspace_layout(a.M, a.K, a.rank);
+    FusedKArgs f;
+    f.e = make_ec_kargs(a.ecargs, L);
+    f.e.ready = (uint32_t*)a.workspace + kEcReadyWord;
+    f.ec_blocks = L.m_tiles * L.splits;
+    f.E = (int)round_up(f.ec_blocks, 8);
+    f.sync = sync;
+    k.P = f.e.P_out;
+    k.g = f.e.g_out;
+    k.ready = f.e.ready;
+    k.ec_tiles = L.m_tiles;
+    f.g = k;
+    if (t.tm == 256 && t.tn == 224) return launch_fused<8, 7, 2, 2, false>(f, stream);
+    if (t.tm == 256) return launch_fused<8, 8, 2, 2, false>(f, stream);
+    if (t.tm == 128) return launch_fused<4, 4, 2, 2, true>(f, stream);
+    return launch_fused<2, 4, 2, 2, true>(f, stream);
+  }
   // 256-row tiles never split; the mid-size tiles are built with the split
   // path, which they skip when S is 1.
   if (t.tm == 256 && t.tn == 224) return launch_cfg<8, 7, 2, 2, false>(k, stream);

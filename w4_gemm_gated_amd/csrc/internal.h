@@ -39,13 +39,23 @@ constexpr size_t kGemmSyncOffset = 32 * 1024;
 constexpr size_t kHandoffOffset = 64 * 1024;
 constexpr size_t kHandoffBytes = 192 * 1024;
 constexpr int64_t kMaxSyncWords = 8192;   // per counter region
+// Words of the GEMM counter region ([32 KiB, 64 KiB)), each hot one on its own
+// 128-byte line: fused finisher count, error flag, call epoch (advanced by
+// every fused call), then split-K tile counters.
+constexpr int kSyncFinishers = 32, kSyncError = 64, kSyncEpoch = 96, kSyncTiles = 128;
+// EC counter region ([0, 32 KiB)): row-tile counters in words [0, 4096), the
+// fused tiled launch's ready flags (raised to the call's epoch + 1) in words
+// [4096, 8192).
+constexpr int kEcReadyWord = 4096;
+constexpr int64_t kMaxEcTiles = 4096;
 
 // Workspace layout of the EC projection (offsets in bytes, 256-aligned).
 struct EcWorkspace {
   int32_t m_tiles = 0;   // row tiles of the projection
   int32_t tile_rows = 0; // rows per tile (16 or 64)
   int32_t splits = 0;    // K slices
-  int32_t k_slice = 0;   // k per slice (multiple of 32)
+  int32_t k_slice = 0;   // k per slice (multiple of the sub-slab)
+  int32_t ss = 0;        // k per sub-slab (256, 128 or 64 by rank)
   size_t counters = 0;   // uint32 [m_tiles]
   size_t partials = 0;   // float [splits][m_tiles * tile_rows][ec_cols]
   size_t p = 0;          // float [M][p_stride]
@@ -88,6 +98,8 @@ struct GemmArgs {
   int32_t ec;          // apply the gated EC term
   void* workspace;     // base (split partials and tile counters), may be null without splits
   size_t scratch_base; // first workspace byte the GEMM may use as scratch
+  int32_t fused;       // P and g computed by EC workgroups of the same launch
+  EcArgs ecargs;       // fused: the projection's arguments (P and g in the EC workspace)
 };
 
 // Skinny (M <= 16) kernel: tile shape, producers and workspace layout.

@@ -4,10 +4,11 @@
 //
 // Decisions:
 //   * no EC (rank 0) or variant NO_EC            -> NO_EC: the W4 GEMM alone;
-//   * AUTO, M <= 16 rows and rank % 4 == 0       -> FUSED: one launch (EC
-//     producers, split-K W4 GEMM, gated epilogue);
-//   * AUTO otherwise (M > 16, or rank % 4 != 0)  -> SPLIT (EC projection
-//     launch, then the tiled GEMM with the gated epilogue);
+//   * AUTO and rank % 4 == 0                     -> FUSED: one launch (EC
+//     workgroups first, then the W4 GEMM with the gated epilogue, which
+//     waits for the EC results it needs);
+//   * AUTO otherwise (rank % 4 != 0)             -> SPLIT (EC projection
+//     launch, then the W4 GEMM with the gated epilogue);
 //   * the per-token gate-value decision (skip the EC term where every gate of
 //     a wave's rows is below tau) is taken on the device in the epilogue.
 //   * main kernel family by M: skinny (M <= 16 rows) or tiled (256-row tiles;
@@ -42,10 +43,13 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   p.cus = cus;
   const bool skinny = d.M <= kSkinnyMaxM;
   const bool ec = d.rank > 0 && d.variant != SPEAR_VARIANT_NO_EC;
-  // The fused producers read A with 8-byte transposing LDS reads: rank % 4 == 0.
+  // The fused EC workgroups copy A rows verbatim (16-byte units) and read it
+  // with 8-byte transposing LDS reads: rank % 4 == 0.
   auto fused_ok = [&]() {
-    if (!skinny || d.rank % 4 != 0) return false;
-    return skinny_shape(d.M, d.K, d.N, d.rank, true, cus, kSyncHeaderBytes).fits;
+    if (d.rank % 4 != 0) return false;
+    if (skinny) return skinny_shape(d.M, d.K, d.N, d.rank, true, cus, kSyncHeaderBytes).fits;
+    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank);
+    return L.m_tiles <= kMaxEcTiles;
   };
   if (!ec) {
     p.variant = SPEAR_VARIANT_NO_EC;
@@ -57,13 +61,18 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   if (p.variant == SPEAR_VARIANT_FUSED && !fused_ok()) return SPEAR_ERR_UNSUPPORTED;
   size_t ws = 0;
   size_t scratch_base = kSyncHeaderBytes;
-  if (p.variant == SPEAR_VARIANT_SPLIT) {
+  // The EC projection's workspace: the split variant's first launch, or the
+  // fused tiled launch's EC workgroups.
+  const bool ec_ws = p.variant == SPEAR_VARIANT_SPLIT || (p.variant == SPEAR_VARIANT_FUSED && !skinny);
+  int ec_blocks = 0;
+  if (ec_ws) {
     const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank);
-    if (L.m_tiles > kMaxSyncWords) return SPEAR_ERR_UNSUPPORTED;
+    if (L.m_tiles > kMaxEcTiles) return SPEAR_ERR_UNSUPPORTED;
     ws = L.bytes;
     scratch_base = L.bytes;
     p.ec_split = L.splits;
     p.producers = L.m_tiles * L.splits;
+    ec_blocks = (int)round_up(p.producers, 8);
   }
   if (skinny) {
     const SkinnyShape sh = skinny_shape(d.M, d.K, d.N, d.rank, p.variant == SPEAR_VARIANT_FUSED, cus,
@@ -88,7 +97,8 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     p.kernel = 1;
     p.tile_m = t.tm; p.tile_n = t.tn;
     p.split_k = t.split;
-    p.grid = t.grid;
+    // Fused: the EC workgroups (padded to a multiple of 8) lead the grid.
+    p.grid = t.grid + (p.variant == SPEAR_VARIANT_FUSED ? ec_blocks : 0);
     if (t.ws_bytes > ws) ws = t.ws_bytes;
   }
   p.workspace_bytes = d.M > 0 ? ws : 0;

@@ -42,7 +42,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Sync words of the GEMM half of the counter header, each hot one on its own
 // 128-byte line (pollers and updaters of different words never share one).
-constexpr int kFinishers = 32, kError = 64, kEpoch = 96, kTiles = 128;
+constexpr int kFinishers = kSyncFinishers, kError = kSyncError, kEpoch = kSyncEpoch, kTiles = kSyncTiles;
 
 struct SkinnyKArgs {
   const half_t* X;
