@@ -198,6 +198,20 @@ def test_tiled_ragged_shapes(M, K, N, r, variant):
     layer_case(X, W, A, B, w_g, -0.5, 0.0, variant, f"tiled {variant} M={M} K={K} N={N} r={r}")
 
 
+@pytest.mark.parametrize("variant", ["fused", "split", "no_ec"])
+@pytest.mark.parametrize("M,K,N,r", [(2100, 1000, 7000, 36), (1500, 520, 7168, 64)])
+def test_large_tile_ragged_shapes(M, K, N, r, variant):
+    """The 256-row tiles (256 x 256 and 256 x 224) on a partial last row
+    tile, a K tail, a partial last column tile and a partial 32-column group;
+    sampled rows, the last rows included."""
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=7 * M + K + N + r, outliers=True)
+    if variant == "no_ec":
+        A = B = w_g = None
+    rows = np.sort(np.random.default_rng(M).choice(M, 40, replace=False))
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rows]))
+    layer_case(X, W, A, B, w_g, -0.5, 0.0, variant, f"large-tile {variant} M={M} K={K} N={N} r={r}", rows=rows)
+
+
 def test_empty_batch():
     w = workloads.workload(1)
     Wq_d, s_d = sp.spear_pack_w4(cuda(w["W"]))

@@ -34,12 +34,19 @@ __device__ __forceinline__ float4_t mfma16x16x32(const half8_t& a, const half8_t
 // 0,2,4,6,1,3,5,7) into the eight fp16 values q = u - 8 in k order.
 // OR-ing 0x6400 into a 16-bit half holding u (< 16) in its low mantissa bits
 // gives exactly the fp16 value 1024 + u; subtracting 1032 leaves u - 8.
+// (x & m) | e in one instruction (the compiler emits an AND and an OR).
+// One scalar operand at most (one constant-bus read per instruction).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "s"(m), "v"(e));
+  return d;
+}
 __device__ __forceinline__ half8_t decode_w4(uint32_t w) {
   const uint32_t m = 0x000F000Fu, e = 0x64006400u;
-  const uint32_t d0 = (w & m) | e;
-  const uint32_t d1 = ((w >> 4) & m) | e;
-  const uint32_t d2 = ((w >> 8) & m) | e;
-  const uint32_t d3 = ((w >> 12) & m) | e;
+  const uint32_t d0 = and_or(w, m, e);
+  const uint32_t d1 = and_or(w >> 4, m, e);
+  const uint32_t d2 = and_or(w >> 8, m, e);
+  const uint32_t d3 = and_or(w >> 12, m, e);
   const half2_t bias = {(half_t)1032.0f, (half_t)1032.0f};
   const half2_t h0 = __builtin_bit_cast(half2_t, d0) - bias;
   const half2_t h1 = __builtin_bit_cast(half2_t, d1) - bias;

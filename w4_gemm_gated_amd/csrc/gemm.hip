@@ -79,6 +79,80 @@ __device__ __forceinline__ void copy2_to_lds(const void* src, void* dst_wave_bas
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 2, 0, 0);
 }
 
+// ---- gated EC epilogue pieces shared by the tile kernels.  The LDS (free
+// once every wave is done with the X stages) holds, per 64-column chunk of
+// the rank, the B rows bs[64][TN] (dword slots, fp16 in the low half; rows
+// >= rank clamped: they meet zero P columns) and pg[TM][64] = fp16(g' P) of
+// the tile's rows (rows >= M clamped: never stored), after gs[TM], the
+// tile's gates.
+template <int TN>
+__device__ __forceinline__ size_t ec_pg_offset() { return (size_t)kEcChunk * TN * 4; }
+template <int TM, int TN>
+__device__ __forceinline__ size_t ec_gs_offset() { return (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2; }
+
+// Fused launch: wait until the EC row tiles under rows [m0, m0 + TM) are
+// published (one thread polls).  Then (every launch) gs[TM] = g' of the
+// tile's rows, 0 past M.  Starts and ends with a block-wide barrier.
+template <int TM, bool FUSED>
+__device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t tag, float* gs) {
+  const int tid = threadIdx.x;
+  if (FUSED && tid == 0) {
+    const int t_end = min(a.ec_tiles, (m0 + TM + 63) / 64);
+    for (int t = m0 / 64; t < t_end; ++t) {
+      uint32_t n = 0;
+      while (ld_dev_u32(&a.ready[t]) != tag) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++n > a.spin_limit) {
+          st_dev_u32(a.error, 1u);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();                             // also: every wave is done with the X stages
+  if (tid < TM) gs[tid] = m0 + tid < a.M ? (FUSED ? ld_dev(&a.g[m0 + tid]) : a.g[m0 + tid]) : 0.0f;
+  __syncthreads();
+}
+
+// Stage rank columns [j0, j0 + 64) of the EC operands: bs (direct copies)
+// and pg (every P load of the chunk issued before the first is used: one
+// memory round trip; device-coherent when the same launch produced P).
+// Ends with the copies landed and a block-wide barrier.
+template <int TM, int TN, bool FUSED>
+__device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m0, int n0, unsigned char* lds,
+                                               __amdgpu_buffer_rsrc_t pr) {
+  constexpr int kPUnits = TM * (kEcChunk / 4) / kGemmThreads;   // 16-byte P units per thread
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  uint32_t* bs = reinterpret_cast<uint32_t*>(lds);
+  half_t* pg = reinterpret_cast<half_t*>(lds + ec_pg_offset<TN>());
+  const float* gs = reinterpret_cast<const float*>(lds + ec_gs_offset<TM, TN>());
+  __syncthreads();
+  for (int e = w * kWave; e < kEcChunk * TN; e += 4 * kWave) {
+    const int idx = e + lane, r = idx / TN, c = idx % TN;
+    copy2_to_lds(a.B + (size_t)min(j0 + r, a.rank - 1) * a.N + min(n0 + c, a.N - 1), bs + e);
+  }
+  float4_t pv[kPUnits];
+#pragma unroll
+  for (int i = 0; i < kPUnits; ++i) {
+    const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
+    const int row = min(m0 + r, a.M - 1), col = j0 + c4 * 4;
+    const uint32_t off = col < a.ps ? (uint32_t)(((size_t)row * a.ps + col) * 4) : kOutOfRange;
+    pv[i] = FUSED ? buffer_load_f4_dev(pr, off)
+                  : __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
+  }
+#pragma unroll
+  for (int i = 0; i < kPUnits; ++i) {
+    const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
+    const float gv = gs[r];
+    half_t* dst = pg + (size_t)r * kEcChunk + c4 * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = (half_t)(gv * pv[i][e]);
+  }
+  wait_vm_all();
+  __syncthreads();
+}
+
 // One GEMM workgroup (tile block `block`).  Wave tile MBW x NBW blocks of
 // 16 x 16; workgroup WM x WN waves.  SPLIT: K split over a.S workgroups per
 // tile.  FUSED: P and g come from EC workgroups of the same launch; the
@@ -209,13 +283,30 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = zero_float4();
-    for (int sp = 0; sp < a.S; ++sp) {
-      const uint32_t base = (uint32_t)(tile * a.S + sp) * slice;
+    // SB splits per batch, all their loads in flight together (about 32 per
+    // thread): one memory round trip per batch.
+    constexpr int SB = MBW * NBW >= 32 ? 1 : 32 / (MBW * NBW);
+    for (int sp0 = 0; sp0 < a.S; sp0 += SB) {
+      float4_t v[SB][MBW][NBW];
 #pragma unroll
-      for (int mb = 0; mb < MBW; ++mb)
+      for (int q = 0; q < SB; ++q) {
+        const bool in = sp0 + q < a.S;
+        const uint32_t base = (uint32_t)(tile * a.S + sp0 + q) * slice;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-          acc[mb][nb] += buffer_load_f4_dev(pr, base + (uint32_t)((mb * NBW + nb) * kGemmThreads + tid) * 16u);
+        for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb)
+            v[q][mb][nb] = buffer_load_f4_dev(
+                pr, in ? base + (uint32_t)((mb * NBW + nb) * kGemmThreads + tid) * 16u : kOutOfRange);
+      }
+#pragma unroll
+      for (int q = 0; q < SB; ++q)
+        if (sp0 + q < a.S) {
+#pragma unroll
+          for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] += v[q][mb][nb];
+        }
     }
   }
 
@@ -233,65 +324,20 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] *= s;
   }
   const int jblocks = a.ec ? a.ps / 32 : 0;
-  uint32_t* bs = reinterpret_cast<uint32_t*>(lds);
-  half_t* pg = reinterpret_cast<half_t*>(lds + (size_t)kEcChunk * TN * 4);
-  float* gs = reinterpret_cast<float*>(lds + (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2);
+  const uint32_t* bs = reinterpret_cast<const uint32_t*>(lds);
+  const half_t* pg = reinterpret_cast<const half_t*>(lds + ec_pg_offset<TN>());
+  float* gs = reinterpret_cast<float*>(lds + ec_gs_offset<TM, TN>());
   bool any_gate = false;
   if (jblocks > 0) {
-    if (FUSED && tid == 0) {
-      // Wait until the EC row tiles under this tile's rows are published.
-      const int t_end = min(a.ec_tiles, (m0 + TM + 63) / 64);
-      for (int t = m0 / 64; t < t_end; ++t) {
-        uint32_t n = 0;
-        while (ld_dev_u32(&a.ready[t]) != tag) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++n > a.spin_limit) {
-            st_dev_u32(a.error, 1u);
-            break;
-          }
-        }
-      }
-    }
-    __syncthreads();                           // also: every wave is done with the X stages
-    // gs[TM] = g' of the tile's rows (0 past M), one load per thread.
-    if (tid < TM) gs[tid] = m0 + tid < a.M ? (FUSED ? ld_dev(&a.g[m0 + tid]) : a.g[m0 + tid]) : 0.0f;
-    __syncthreads();
+    ec_prepare<TM, FUSED>(a, m0, tag, gs);
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) any_gate |= gs[wm * MBW * 16 + mb * 16 + c16] != 0.0f;
     any_gate = __any(any_gate);
   }
-  // P through a buffer resource (columns >= ps read as zeros): device-coherent
-  // loads when the same launch produced it.
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((size_t)a.M * a.ps * 4));
-  constexpr int kPUnits = TM * (kEcChunk / 4) / kGemmThreads;   // 16-byte P units per thread per chunk
   const int n0 = n_tile * TN;
   for (int j0 = 0; j0 < jblocks * 32; j0 += kEcChunk) {
-    __syncthreads();
-    for (int e = w * kWave; e < kEcChunk * TN; e += 4 * kWave) {
-      const int idx = e + lane, r = idx / TN, c = idx % TN;
-      copy2_to_lds(a.B + (size_t)min(j0 + r, a.rank - 1) * a.N + min(n0 + c, a.N - 1), bs + e);
-    }
-    // pg[TM][64] = fp16(g' P): every P load of the chunk is issued before the
-    // first is used (one memory round trip).
-    float4_t pv[kPUnits];
-#pragma unroll
-    for (int i = 0; i < kPUnits; ++i) {
-      const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
-      const int row = min(m0 + r, a.M - 1), col = j0 + c4 * 4;
-      const uint32_t off = col < a.ps ? (uint32_t)(((size_t)row * a.ps + col) * 4) : kOutOfRange;
-      pv[i] = FUSED ? buffer_load_f4_dev(pr, off)
-                    : __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
-    }
-#pragma unroll
-    for (int i = 0; i < kPUnits; ++i) {
-      const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
-      const float gv = gs[r];
-      half_t* dst = pg + (size_t)r * kEcChunk + c4 * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = (half_t)(gv * pv[i][e]);
-    }
-    wait_vm_all();
-    __syncthreads();
+    ec_stage_chunk<TM, TN, FUSED>(a, j0, m0, n0, lds, pr);
     if (any_gate) {
       const int jbn = min(kEcChunk, jblocks * 32 - j0) / 32;
       for (int jb = 0; jb < jbn; ++jb) {
@@ -328,9 +374,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   }
 }
 
-template <int MBW, int NBW, int WM, int WN>
-constexpr size_t tile_lds_bytes() {
-  constexpr int TM = 16 * MBW * WM, TN = 16 * NBW * WN;
+template <int TM, int TN>
+constexpr size_t lds_bytes_for() {
   constexpr size_t stages = (size_t)2 * TM * kKt * 2;
   constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
   return stages > epilogue ? stages : epilogue;
@@ -372,7 +417,7 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs 
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT>
 hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
-  constexpr size_t lds = tile_lds_bytes<MBW, NBW, WM, WN>();
+  constexpr size_t lds = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN>();
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -384,7 +429,7 @@ hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB>
 hipError_t launch_fused_pb(const FusedKArgs& f, void* stream) {
-  const size_t tile = tile_lds_bytes<MBW, NBW, WM, WN>(), ec = ec_lds_bytes(f.e.ss, f.e.rp);
+  const size_t tile = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN>(), ec = ec_lds_bytes(f.e.ss, f.e.rp);
   const size_t lds = tile > ec ? tile : ec;
   if (ec_kb_for(PB) * 32 != f.e.ss || lds > kMaxLdsBytes - 1024) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
