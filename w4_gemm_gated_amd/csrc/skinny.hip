@@ -211,16 +211,25 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
     float4_t acc[kPass];
 #pragma unroll
     for (int j = 0; j < kPass; ++j) acc[j] = zero_float4();
-    for (int i = 0; i < kbw; ++i) {
-      const int kb = w + 4 * i;
-      const half8_t xf = *reinterpret_cast<const half8_t*>(xrow + (size_t)(((kb * 4 + t4) ^ c16) * 8));
-      half8_t bf[kPass];
+    // Every LDS fragment read of the pass is issued before the first matrix
+    // instruction (kbw <= 8: ksp <= 1024; reads past kbw repeat the last
+    // block and are not used).
+    constexpr int kMaxKbw = 8;
+    half8_t xf[kMaxKbw], bf[kMaxKbw][kPass];
+#pragma unroll
+    for (int i = 0; i < kMaxKbw; ++i) {
+      const int kb = w + 4 * min(i, kbw - 1);
+      xf[i] = *reinterpret_cast<const half8_t*>(xrow + (size_t)(((kb * 4 + t4) ^ c16) * 8));
 #pragma unroll
       for (int j = 0; j < kPass; ++j)
-        bf[j] = lds_b_fragment_tr(bsrc[j] + (size_t)kb * 32 * bstride[j], bstride[j], lane);
-#pragma unroll
-      for (int j = 0; j < kPass; ++j) acc[j] = mfma16x16x32(xf, bf[j], acc[j]);
+        bf[i][j] = lds_b_fragment_tr(bsrc[j] + (size_t)kb * 32 * bstride[j], bstride[j], lane);
     }
+#pragma unroll
+    for (int i = 0; i < kMaxKbw; ++i)
+      if (i < kbw) {
+#pragma unroll
+        for (int j = 0; j < kPass; ++j) acc[j] = mfma16x16x32(xf[i], bf[i][j], acc[j]);
+      }
     __syncthreads();                           // every wave is done with the X slab / last pass
 #pragma unroll
     for (int j = 0; j < kPass; ++j) red[(w * kPass + j) * kWave + lane] = acc[j];
@@ -250,8 +259,7 @@ constexpr size_t static_lds_bytes(int nbw) { return (size_t)3 * kWave * nbw * 16
 
 // Dynamic LDS of a GEMM workgroup with the EC on: the EC factor tile
 // Bs[jblocks*32][TN] (fp16); Pc[16][rank + 1] floats (P, then the final gate
-// g'); then the fused variant's copy of the hand-off slabs Ht[P][M][r1p] or
-// the split variant's Pt[16][ps] floats and gt[16].
+// g'); then, split variant, Pt[16][ps] floats and gt[16].
 //
 // The EC operands that are ready at the start (the B tile, the split
 // variant's P and g) are loaded into registers ahead of the weight stream, a
@@ -267,10 +275,91 @@ __host__ __device__ __forceinline__ size_t gemm_bs_bytes(int ps, int tn) {
 }
 __host__ __device__ __forceinline__ size_t gemm_pc_bytes(int rank) { return ((size_t)16 * (rank + 1) * 4 + 15) & ~(size_t)15; }
 __host__ __device__ __forceinline__ size_t gemm_table_bytes(int ec_mode, int ps, int r1p, int P, int M) {
-  if (ec_mode == 1) {
-    return (size_t)P * M * r1p * 8;
-  }
+  if (ec_mode == 1) return 0;   // the fused hand-off is summed in registers
   return (size_t)16 * ps * 4 + 16 * 4;
+}
+
+// Fused consumer: the final [P | g'] of this call from the producers' slabs.
+// Thread t takes 16-byte units q = t, t + 256, ... of a slab (two entries of
+// row q / (r1p / 2)) and loads that unit of every slab, Q units x PB slabs
+// in flight at once (one memory round trip per batch); units whose tag is
+// not yet this call's are reloaded (bounded wait).  The slabs are added in
+// fixed order and the gate applied to column rank.
+template <int Q, int PB>
+__device__ void gather_handoff(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, uint32_t tag, float* Pc) {
+  const int tid = threadIdx.x;
+  const int r1 = a.rank + 1;
+  const int pairs = a.M * a.r1p / 2;                     // 16-byte units per slab
+  const uint32_t slab_bytes = (uint32_t)a.M * (uint32_t)a.r1p * 8u;
+  for (int q0 = 0; q0 < pairs; q0 += Q * kThreads) {
+    float s0[Q], s1[Q];
+#pragma unroll
+    for (int i = 0; i < Q; ++i) s0[i] = s1[i] = 0.0f;
+    for (int p0 = 0; p0 < a.P; p0 += PB) {
+      u32x4_t v[Q][PB];
+      auto offset = [&](int i, int j) -> uint32_t {
+        const int q = q0 + i * kThreads + tid;
+        return (q < pairs && p0 + j < a.P) ? (uint32_t)(p0 + j) * slab_bytes + (uint32_t)q * 16u : kOutOfRange;
+      };
+      // Entry 1 of a unit past column rank is never written (tag 0).
+      auto ready = [&](int i, const u32x4_t& u) -> bool {
+        const int c0 = (2 * (q0 + i * kThreads + tid)) % a.r1p;
+        return u[1] == tag && (c0 + 1 >= r1 || u[3] == tag);
+      };
+#pragma unroll
+      for (int i = 0; i < Q; ++i)
+#pragma unroll
+        for (int j = 0; j < PB; ++j)
+          v[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, offset(i, j), 0,
+                                                                                        kCachePolicySc1));
+      uint32_t n = 0;
+      for (;;) {
+        bool stale = false;
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+#pragma unroll
+          for (int j = 0; j < PB; ++j) stale |= offset(i, j) != kOutOfRange && !ready(i, v[i][j]);
+        if (!stale) break;
+        if (++n > a.spin_limit) {
+          st_dev_u32(&a.sync[kError], 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+#pragma unroll
+          for (int j = 0; j < PB; ++j)
+            if (offset(i, j) != kOutOfRange && !ready(i, v[i][j]))
+              v[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, offset(i, j), 0,
+                                                                                            kCachePolicySc1));
+      }
+#pragma unroll
+      for (int i = 0; i < Q; ++i)
+#pragma unroll
+        for (int j = 0; j < PB; ++j)
+          if (p0 + j < a.P) {
+            s0[i] += bits_float(v[i][j][0]);
+            s1[i] += bits_float(v[i][j][2]);
+          }
+    }
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int q = q0 + i * kThreads + tid;
+      if (q >= pairs) continue;
+      const int row = (2 * q) / a.r1p, c0 = (2 * q) % a.r1p;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int col = c0 + e;
+        if (col >= r1) continue;
+        float v = e == 0 ? s0[i] : s1[i];
+        if (col == a.rank) {
+          v = sigmoidf_(v + a.gate_bias);
+          if (a.skip_tau > 0.0f && !(v >= a.skip_tau)) v = 0.0f;
+        }
+        Pc[row * r1 + col] = v;
+      }
+    }
+  }
 }
 
 // EXACT: every wave owns exactly CPW chunks (no validity test, so no load
@@ -369,7 +458,6 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
       for (int j = 0; j < 4; ++j) xa[c][j] = zero_half8();
     }
   }
-  const int handoff_units = ECM == 1 ? a.P * a.M * a.r1p / 2 : 0;   // 16-byte units, two entries each
   // Keep every load above this point (no load may sink into the
   // matrix-instruction block and pay a second round trip).
   __builtin_amdgcn_sched_barrier(0);
@@ -460,79 +548,17 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
     }
   }
 
-  // ---- fused: complete the hand-off copy and check its tags; units that
-  // were not yet published are reloaded (bounded wait).
+  // ---- fused: gather the producers' slabs, check their tags (units not yet
+  // published are reloaded, bounded wait), add them and apply the gate.
   if (ECM == 1) {
-    uint64_t* Ht = reinterpret_cast<uint64_t*>(table);
-    u32x4_t* Hu = reinterpret_cast<u32x4_t*>(table);
-    const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.handoff, (uint32_t)((size_t)handoff_units * 16));
-    // A unit (two entries) is ready when every entry of it that the producers
-    // write (columns < rank + 1) carries this call's tag.
-    auto unit_ready = [&](const u32x4_t& v, int u) {
-      const int e0 = 2 * u;
-      const bool ok0 = e0 % a.r1p >= r1 || v[1] == tag;
-      const bool ok1 = (e0 + 1) % a.r1p >= r1 || v[3] == tag;
-      return ok0 && ok1;
-    };
-    // The whole table, after the matrix instructions: batches of sixteen
-    // loads per thread.  (Requested any earlier, the loads would queue
-    // behind the weight stream and be served about when it is, normally just
-    // before the producers publish, which costs a second round trip.)
-    for (int u0 = 0; u0 < handoff_units; u0 += 16 * kThreads) {
-      u32x4_t v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int u = u0 + i * kThreads + tid;
-        v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                               hr, u < handoff_units ? (uint32_t)u * 16u : kOutOfRange, 0,
-                                               kCachePolicySc1));
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int u = u0 + i * kThreads + tid;
-        if (u < handoff_units) Hu[u] = v[i];
-      }
-    }
-    // Units not yet published: reload, up to sixteen at a time per thread,
-    // until ready (bounded).
-    uint32_t n = 0;
-    for (;;) {
-      bool stale = false;
-      int pend[16];
-      int np = 0;
-      for (int u = tid; u < handoff_units && np < 16; u += kThreads)
-        if (!unit_ready(Hu[u], u)) pend[np++] = u;
-      stale = np > 0;
-      if (!__syncthreads_or(stale)) break;
-      if (++n > a.spin_limit) {
-        if (tid == 0) st_dev_u32(&a.sync[kError], 1u);
-        break;
-      }
-      if (np > 0) {
-        if (n > 1) __builtin_amdgcn_s_sleep(4);
-        u32x4_t v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 hr, i < np ? (uint32_t)pend[i] * 16u : kOutOfRange, 0,
-                                                 kCachePolicySc1));
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < np) Hu[pend[i]] = v[i];
-      }
-    }
-    // Add the slabs in fixed order into Pc, with the gate applied.
-    for (int idx = tid; idx < a.M * r1; idx += kThreads) {
-      const int row = idx / r1, col = idx % r1;
-      float v = 0.0f;
-      for (int p = 0; p < a.P; ++p)
-        v += bits_float((uint32_t)Ht[((size_t)p * a.M + row) * a.r1p + col]);
-      if (col == a.rank) {
-        v = sigmoidf_(v + a.gate_bias);
-        if (a.skip_tau > 0.0f && !(v >= a.skip_tau)) v = 0.0f;
-      }
-      Pc[idx] = v;
-    }
+    const __amdgpu_buffer_rsrc_t hr =
+        make_rsrc(a.handoff, (uint32_t)((size_t)a.P * a.M * a.r1p * 8));
+    // The whole table after the matrix instructions.  (Requested any
+    // earlier, the loads would queue behind the weight stream and be served
+    // about when it is, normally just before the producers publish, which
+    // costs a second round trip.)  Sixteen loads in flight per thread.
+    if (a.P <= 8) gather_handoff<2, 8>(a, hr, tag, Pc);
+    else gather_handoff<1, 16>(a, hr, tag, Pc);
     __syncthreads();
     // Count this workgroup out (wave 1, off wave 0's path): the last one
     // returns the counters to zero and advances the epoch (every producer and
