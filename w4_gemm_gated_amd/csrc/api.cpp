@@ -175,7 +175,7 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
   EcArgs e;
   std::memset(&e, 0, sizeof(e));
   if (p.variant == SPEAR_VARIANT_SPLIT || fused_tiled) {
-    L = ec_workspace_layout(desc->M, desc->K, desc->rank);
+    L = ec_workspace_layout(desc->M, desc->K, desc->rank, fused_tiled ? kEcBlocksFused : kEcBlocksSplit);
     ec_bytes = L.bytes;
     e.X = X; e.A = A; e.w_g = w_g;
     e.M = desc->M; e.K = desc->K; e.rank = desc->rank;

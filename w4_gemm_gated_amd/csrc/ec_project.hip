@@ -17,17 +17,17 @@ inline int sub_slab(int64_t rank) {
 
 }  // namespace
 
-EcWorkspace ec_workspace_layout(int64_t M, int64_t K, int64_t rank) {
+EcWorkspace ec_workspace_layout(int64_t M, int64_t K, int64_t rank, int target_blocks) {
   EcWorkspace w;
   if (rank <= 0 || M <= 0) return w;
   w.tile_rows = kEcTileRows;
   w.m_tiles = (int32_t)ceil_div(M, kEcTileRows);
-  // K slices: enough workgroups to spread the read of X over the GPU (about
-  // 256), at most 16 slices (the last arriver of a row tile adds them all).
+  // K slices: about target_blocks workgroups, at most 16 slices (the last
+  // arriver of a row tile adds them all).
   const int ss = sub_slab(rank);
   w.ss = ss;
   const int64_t max_splits = ceil_div(K, ss);
-  int64_t splits = ceil_div(256, w.m_tiles);
+  int64_t splits = ceil_div(target_blocks, w.m_tiles);
   if (splits > 16) splits = 16;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;

@@ -516,7 +516,7 @@ hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream
   if (a.fused) {
     // EC workgroups first (P and g into the EC workspace, ready flags in the
     // EC counter region), then the GEMM tiles.
-    const EcWorkspace L = ec_workspace_layout(a.M, a.K, a.rank);
+    const EcWorkspace L = ec_workspace_layout(a.M, a.K, a.rank, kEcBlocksFused);
     FusedKArgs f;
     f.e = make_ec_kargs(a.ecargs, L);
     f.e.ready = (uint32_t*)a.workspace + kEcReadyWord;

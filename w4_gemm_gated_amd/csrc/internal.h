@@ -62,7 +62,12 @@ struct EcWorkspace {
   size_t g = 0;          // float [M]
   size_t bytes = 0;
 };
-EcWorkspace ec_workspace_layout(int64_t M, int64_t K, int64_t rank);
+// target_blocks: about how many workgroups the K slices should give (the
+// split variant's own launch spreads the read of X over the GPU; the fused
+// tiled launch, whose EC workgroups each hold a CU the GEMM tiles wait for,
+// takes fewer).
+constexpr int kEcBlocksSplit = 256, kEcBlocksFused = 64;
+EcWorkspace ec_workspace_layout(int64_t M, int64_t K, int64_t rank, int target_blocks = kEcBlocksSplit);
 
 // Host planner (pure host code; no HIP calls).
 spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* plan);

@@ -48,7 +48,7 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   auto fused_ok = [&]() {
     if (d.rank % 4 != 0) return false;
     if (skinny) return skinny_shape(d.M, d.K, d.N, d.rank, true, cus, kSyncHeaderBytes).fits;
-    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank);
+    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank, kEcBlocksFused);
     return L.m_tiles <= kMaxEcTiles;
   };
   if (!ec) {
@@ -66,7 +66,8 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   const bool ec_ws = p.variant == SPEAR_VARIANT_SPLIT || (p.variant == SPEAR_VARIANT_FUSED && !skinny);
   int ec_blocks = 0;
   if (ec_ws) {
-    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank);
+    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank,
+                                              p.variant == SPEAR_VARIANT_FUSED ? kEcBlocksFused : kEcBlocksSplit);
     if (L.m_tiles > kMaxEcTiles) return SPEAR_ERR_UNSUPPORTED;
     ws = L.bytes;
     scratch_base = L.bytes;
