@@ -139,5 +139,14 @@ __device__ __forceinline__ void wait_vm_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   asm volatile("" ::: "memory");
 }
+// Wait until at most N of this wave's memory instructions are in flight
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace spear

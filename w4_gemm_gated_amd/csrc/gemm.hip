@@ -28,6 +28,7 @@
 // 16-byte stores) and takes a ticket; the last to arrive adds the S partials
 // in fixed order, so results do not depend on timing, and runs the epilogue.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "ec_block.h"
@@ -153,6 +154,10 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
   __syncthreads();
 }
 
+// X stages of a tile kernel: three (loads two steps ahead) for the 64-row
+// tiles of small M, where the steps are short; two otherwise.
+constexpr int stages_for(int tm, bool split) { return split && tm == 64 ? 3 : 2; }
+
 // One GEMM workgroup (tile block `block`).  Wave tile MBW x NBW blocks of
 // 16 x 16; workgroup WM x WN waves.  SPLIT: K split over a.S workgroups per
 // tile.  FUSED: P and g come from EC workgroups of the same launch; the
@@ -165,7 +170,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   constexpr int TN = 16 * NBW * WN;
   constexpr int kStageHalves = TM * kKt;                    // one X stage
   constexpr int kCopiesPerWave = TM * kUnitsPerRow / kWave / 4;
-  half_t* xs = reinterpret_cast<half_t*>(lds);                // [2][TM][kKt], swizzled units
+  constexpr int NSTAGE = stages_for(TM, SPLIT);             // X stages in LDS
+  half_t* xs = reinterpret_cast<half_t*>(lds);                // [NSTAGE][TM][kKt], swizzled units
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -225,18 +231,10 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = zero_float4();
 
-  u32x4_t wcur[NBW], wnext[NBW];
   const int kc_begin = split * a.CPS, kc_end = min(a.KC, kc_begin + a.CPS);
-  issue_x(kc_begin, 0);
-  load_w(kc_begin, wcur);
-  for (int kc = kc_begin; kc < kc_end; ++kc) {
-    const int st = (kc - kc_begin) & 1;
-    wait_vm_all();
-    __syncthreads();
-    if (kc + 1 < kc_end) {
-      issue_x(kc + 1, st ^ 1);
-      load_w(kc + 1, wnext);
-    }
+  // The matrix instructions of one 128-k step from X stage `st` and the
+  // packed words w.
+  auto compute = [&](int st, const u32x4_t* w_) {
     const half_t* xst = xs + (size_t)st * kStageHalves;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -249,13 +247,81 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       }
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        const half8_t bf = decode_w4(wcur[nb][j]);
+        const half8_t bf = decode_w4(w_[nb][j]);
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = mfma16x16x32(af[mb], bf, acc[mb][nb]);
       }
     }
+  };
+  if (NSTAGE == 2) {
+    // Two stages, loads one step ahead (the 256-row tiles: two X stages fill
+    // the LDS).
+    u32x4_t wcur[NBW], wnext[NBW];
+    issue_x(kc_begin, 0);
+    load_w(kc_begin, wcur);
+    for (int kc = kc_begin; kc < kc_end; ++kc) {
+      const int st = (kc - kc_begin) & 1;
+      wait_vm_all();
+      __syncthreads();
+      if (kc + 1 < kc_end) {
+        issue_x(kc + 1, st ^ 1);
+        load_w(kc + 1, wnext);
+      }
+      compute(st, wcur);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) wcur[nb] = wnext[nb];
+      for (int nb = 0; nb < NBW; ++nb) wcur[nb] = wnext[nb];
+    }
+  } else {
+    // Three stages, loads two steps ahead; the packed weights go through LDS
+    // too (ws[stage][panel][64 lanes][16 bytes], after the X stages), so no
+    // register holds a load in flight and the only waits are the explicit
+    // ones.  Each step issues L copies per wave; at the top of step i those
+    // of step i + 1 may still be in flight, those of step i must have landed.
+    // Past the last step the copies repeat the last chunk into a stage
+    // nothing reads again, so every step issues the same L copies.
+    constexpr int kPanels = NBW * WN;                       // per workgroup
+    constexpr int kWCopies = (kPanels + WM * WN - 1) / (WM * WN);   // per wave
+    constexpr int L = kCopiesPerWave + kWCopies;
+    unsigned char* wsm = lds + (size_t)NSTAGE * kStageHalves * 2;
+    const int pan0 = n_tile * kPanels;
+    auto issue_w = [&](int kc, int st) {
+#pragma unroll
+      for (int c = 0; c < kWCopies; ++c) {
+        const int pl = min(w * kWCopies + c, kPanels - 1);   // extra copies repeat the last panel
+        const uint32_t voff = ((uint32_t)min(pan0 + pl, a.NBLK - 1) * (uint32_t)a.KC * 64u + (uint32_t)lane) * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (lds_void_t*)(wsm + ((size_t)st * kPanels + pl) * 1024), 16, voff, kc * 1024, 0, 0);
+      }
+    };
+    const int nsteps = kc_end - kc_begin;
+    issue_x(kc_begin, 0);
+    issue_w(kc_begin, 0);
+    {
+      const int k1 = min(kc_begin + 1, kc_end - 1);
+      issue_x(k1, 1);
+      issue_w(k1, 1);
+    }
+    for (int i = 0; i < nsteps; ++i) {
+      const int st = i % 3;
+      // This wave's copies of step i have landed; after the barrier every
+      // wave's have.  A plain barrier: the release fence of __syncthreads
+      // would also wait for step i + 1's copies.  The stage refilled below
+      // was last read in step i - 1, whose reads every wave has completed
+      // (their results fed its matrix instructions) before arriving here.
+      wait_vm_le<L>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int kn = min(kc_begin + i + 2, kc_end - 1);
+      issue_x(kn, (i + 2) % 3);
+      issue_w(kn, (i + 2) % 3);
+      u32x4_t wv[NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+        wv[nb] = *reinterpret_cast<const u32x4_t*>(wsm + (((size_t)st * kPanels + wn * NBW + nb) * 64 + lane) * 16);
+      compute(st, wv);
+    }
+    wait_vm_all();   // the repeated copies land before the LDS is reused
   }
 
   // ---------------------------------------------------------------- split K
@@ -374,9 +440,12 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   }
 }
 
-template <int TM, int TN>
+template <int TM, int TN, int NS>
 constexpr size_t lds_bytes_for() {
-  constexpr size_t stages = (size_t)2 * TM * kKt * 2;
+  // X stages, and with three stages the packed-weight stages (TN / 16 panels
+  // of 1 KiB each, one copy per wave at least).
+  constexpr size_t w_stages = NS == 3 ? (size_t)3 * ((TN / 16 + 3) / 4 * 4) * 1024 : 0;
+  constexpr size_t stages = (size_t)NS * TM * kKt * 2 + w_stages;
   constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
   return stages > epilogue ? stages : epilogue;
 }
@@ -417,7 +486,7 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs 
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT>
 hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
-  constexpr size_t lds = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN>();
+  constexpr size_t lds = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, stages_for(16 * MBW * WM, SPLIT)>();
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -429,7 +498,8 @@ hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB>
 hipError_t launch_fused_pb(const FusedKArgs& f, void* stream) {
-  const size_t tile = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN>(), ec = ec_lds_bytes(f.e.ss, f.e.rp);
+  const size_t tile = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, stages_for(16 * MBW * WM, SPLIT)>();
+  const size_t ec = ec_lds_bytes(f.e.ss, f.e.rp);
   const size_t lds = tile > ec ? tile : ec;
   if (ec_kb_for(PB) * 32 != f.e.ss || lds > kMaxLdsBytes - 1024) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(
