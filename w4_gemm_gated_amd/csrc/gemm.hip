@@ -73,23 +73,16 @@ struct FusedKArgs {
   uint32_t* sync;         // GEMM sync words (finishers, epoch)
 };
 
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void copy2_to_lds(const void* src, void* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst_wave_base, 2, 0, 0);
-}
-
 // ---- gated EC epilogue pieces shared by the tile kernels.  The LDS (free
 // once every wave is done with the X stages) holds, per 64-column chunk of
-// the rank, the B rows bs[64][TN] (dword slots, fp16 in the low half; rows
-// >= rank clamped: they meet zero P columns) and pg[TM][64] = fp16(g' P) of
-// the tile's rows (rows >= M clamped: never stored), after gs[TM], the
+// the rank, the B rows bs[64][TN] fp16 (rows >= rank clamped: they meet zero
+// P columns; columns >= N clamped: never stored) and pg[TM][64] = fp16(g' P)
+// of the tile's rows (rows >= M clamped: never stored), after gs[TM], the
 // tile's gates.
 template <int TN>
-__device__ __forceinline__ size_t ec_pg_offset() { return (size_t)kEcChunk * TN * 4; }
+__device__ __forceinline__ size_t ec_pg_offset() { return (size_t)kEcChunk * TN * 2; }
 template <int TM, int TN>
-__device__ __forceinline__ size_t ec_gs_offset() { return (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2; }
+__device__ __forceinline__ size_t ec_gs_offset() { return (size_t)kEcChunk * TN * 2 + (size_t)TM * kEcChunk * 2; }
 
 // Fused launch: wait until the EC row tiles under rows [m0, m0 + TM) are
 // published (one thread polls).  Then (every launch) gs[TM] = g' of the
@@ -115,23 +108,38 @@ __device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t 
   __syncthreads();
 }
 
-// Stage rank columns [j0, j0 + 64) of the EC operands: bs (direct copies)
-// and pg (every P load of the chunk issued before the first is used: one
-// memory round trip; device-coherent when the same launch produced P).
-// Ends with the copies landed and a block-wide barrier.
+// Stage rank columns [j0, j0 + 64) of the EC operands: bs (16-byte loads
+// when B rows are 16-byte aligned, else element-wise) and pg; every load of
+// the chunk is issued before the first is used (one memory round trip), P's
+// device-coherent when the same launch produced it.  Ends with a block-wide
+// barrier.
 template <int TM, int TN, bool FUSED>
 __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m0, int n0, unsigned char* lds,
                                                __amdgpu_buffer_rsrc_t pr) {
   constexpr int kPUnits = TM * (kEcChunk / 4) / kGemmThreads;   // 16-byte P units per thread
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  uint32_t* bs = reinterpret_cast<uint32_t*>(lds);
+  constexpr int kBUnits = kEcChunk * TN / 8 / kGemmThreads;   // 16-byte B units per thread
+  static_assert(kEcChunk * TN / 8 % kGemmThreads == 0, "whole B units per thread");
+  half_t* bs = reinterpret_cast<half_t*>(lds);
   half_t* pg = reinterpret_cast<half_t*>(lds + ec_pg_offset<TN>());
   const float* gs = reinterpret_cast<const float*>(lds + ec_gs_offset<TM, TN>());
+  (void)w; (void)lane;
   __syncthreads();
-  for (int e = w * kWave; e < kEcChunk * TN; e += 4 * kWave) {
-    const int idx = e + lane, r = idx / TN, c = idx % TN;
-    copy2_to_lds(a.B + (size_t)min(j0 + r, a.rank - 1) * a.N + min(n0 + c, a.N - 1), bs + e);
+  const bool bvec = a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0;
+  u32x4_t bv[kBUnits];
+  if (bvec) {
+#pragma unroll
+    for (int i = 0; i < kBUnits; ++i) {
+      const int idx = i * kGemmThreads + tid, r = idx / (TN / 8), c8 = idx % (TN / 8);
+      bv[i] = *reinterpret_cast<const u32x4_t*>(a.B + (size_t)min(j0 + r, a.rank - 1) * a.N +
+                                                 min(n0 + c8 * 8, a.N - 8));
+    }
+  } else {
+    for (int idx = tid; idx < kEcChunk * TN; idx += kGemmThreads) {
+      const int r = idx / TN, c = idx % TN;
+      bs[idx] = a.B[(size_t)min(j0 + r, a.rank - 1) * a.N + min(n0 + c, a.N - 1)];
+    }
   }
   float4_t pv[kPUnits];
 #pragma unroll
@@ -141,6 +149,10 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
     const uint32_t off = col < a.ps ? (uint32_t)(((size_t)row * a.ps + col) * 4) : kOutOfRange;
     pv[i] = FUSED ? buffer_load_f4_dev(pr, off)
                   : __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
+  }
+  if (bvec) {
+#pragma unroll
+    for (int i = 0; i < kBUnits; ++i) reinterpret_cast<u32x4_t*>(bs)[i * kGemmThreads + tid] = bv[i];
   }
 #pragma unroll
   for (int i = 0; i < kPUnits; ++i) {
@@ -390,7 +402,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] *= s;
   }
   const int jblocks = a.ec ? a.ps / 32 : 0;
-  const uint32_t* bs = reinterpret_cast<const uint32_t*>(lds);
+  const half_t* bs = reinterpret_cast<const half_t*>(lds);
   const half_t* pg = reinterpret_cast<const half_t*>(lds + ec_pg_offset<TN>());
   float* gs = reinterpret_cast<float*>(lds + ec_gs_offset<TM, TN>());
   bool any_gate = false;
@@ -409,11 +421,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       for (int jb = 0; jb < jbn; ++jb) {
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-          const int lc = (wn * NBW + nb) * 16 + c16;
-          half8_t bb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            bb[e] = __builtin_bit_cast(half_t, (uint16_t)bs[(jb * 32 + t4 * 8 + e) * TN + lc]);
+          // B operand rows jb*32 + 8 t4 .. + 7 of column (wn NBW + nb) 16 + c16.
+          const half8_t bb = lds_b_fragment_tr(bs + (size_t)jb * 32 * TN + (wn * NBW + nb) * 16, TN, lane);
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
             const int r = wm * MBW * 16 + mb * 16 + c16;
@@ -425,17 +434,35 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     }
   }
 
+  // ---- Y through LDS: each wave writes its fp16 results into ys[TM][YS],
+  // then the workgroup stores whole rows, 16 bytes per thread and store when
+  // Y rows are 16-byte aligned (N % 8 == 0), else element by element along
+  // the rows.
+  constexpr int YS = TN + 8;                   // row stride (halves), off the bank period
+  half_t* ys = reinterpret_cast<half_t*>(lds);
+  __syncthreads();                             // every wave is done with the epilogue LDS
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int col = (nb_base + nb) * 16 + c16;
-    if (col >= a.N) continue;
+  for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
+    for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * MBW * 16 + mb * 16 + 4 * t4 + v;
-        if (row < a.M) a.Y[(size_t)row * a.N + col] = (half_t)acc[mb][nb][v];
-      }
+      for (int v = 0; v < 4; ++v)
+        ys[(wm * MBW * 16 + mb * 16 + 4 * t4 + v) * YS + (wn * NBW + nb) * 16 + c16] = (half_t)acc[mb][nb][v];
+  __syncthreads();
+  const int rows = min(TM, a.M - m0);
+  if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) {
+    const int cols8 = min(TN, a.N - n0) / 8;
+    for (int idx = tid; idx < rows * (TN / 8); idx += kGemmThreads) {
+      const int r = idx / (TN / 8), c8 = idx % (TN / 8);
+      if (c8 < cols8)
+        *reinterpret_cast<u32x4_t*>(a.Y + (size_t)(m0 + r) * a.N + n0 + c8 * 8) =
+            *reinterpret_cast<const u32x4_t*>(ys + r * YS + c8 * 8);
+    }
+  } else {
+    const int cols = min(TN, a.N - n0);
+    for (int idx = tid; idx < rows * TN; idx += kGemmThreads) {
+      const int r = idx / TN, c = idx % TN;
+      if (c < cols) a.Y[(size_t)(m0 + r) * a.N + n0 + c] = ys[r * YS + c];
     }
   }
 }
@@ -447,7 +474,9 @@ constexpr size_t lds_bytes_for() {
   constexpr size_t w_stages = NS == 3 ? (size_t)3 * ((TN / 16 + 3) / 4 * 4) * 1024 : 0;
   constexpr size_t stages = (size_t)NS * TM * kKt * 2 + w_stages;
   constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
-  return stages > epilogue ? stages : epilogue;
+  constexpr size_t y_tile = (size_t)TM * (TN + 8) * 2;
+  constexpr size_t m = stages > epilogue ? stages : epilogue;
+  return m > y_tile ? m : y_tile;
 }
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT>
