@@ -84,15 +84,34 @@ __device__ __forceinline__ size_t ec_pg_offset() { return (size_t)kEcChunk * TN 
 template <int TM, int TN>
 __device__ __forceinline__ size_t ec_gs_offset() { return (size_t)kEcChunk * TN * 2 + (size_t)TM * kEcChunk * 2; }
 
-// Fused launch: wait until the EC row tiles under rows [m0, m0 + TM) are
-// published (one thread polls).  Then (every launch) gs[TM] = g' of the
-// tile's rows, 0 past M.  Starts and ends with a block-wide barrier.
+// Fused launch: the ready flags of the EC row tiles under rows
+// [m0, m0 + TM), read by thread 0 when the workgroup starts (TM / 64 <= 4
+// of them; those already raised then need no second look).
 template <int TM, bool FUSED>
-__device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t tag, float* gs) {
+__device__ __forceinline__ void ec_flags_early(const GemmKArgs& a, int m0, uint32_t (&early)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) early[i] = 0;
+  if (FUSED && a.ec && threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < (TM + 63) / 64; ++i)
+      if (m0 / 64 + i < a.ec_tiles) early[i] = ld_dev_u32(&a.ready[m0 / 64 + i]);
+  }
+}
+
+// Fused launch: wait until the EC row tiles under rows [m0, m0 + TM) are
+// published (one thread polls the flags not seen raised early).  Then (every
+// launch) gs[TM] = g' of the tile's rows, 0 past M.  Starts and ends with a
+// block-wide barrier.
+template <int TM, bool FUSED>
+__device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t tag, float* gs,
+                                           const uint32_t (&early)[4]) {
   const int tid = threadIdx.x;
   if (FUSED && tid == 0) {
     const int t_end = min(a.ec_tiles, (m0 + TM + 63) / 64);
-    for (int t = m0 / 64; t < t_end; ++t) {
+#pragma unroll
+    for (int i = 0; i < (TM + 63) / 64; ++i) {
+      const int t = m0 / 64 + i;
+      if (t >= t_end || early[i] == tag) continue;
       uint32_t n = 0;
       while (ld_dev_u32(&a.ready[t]) != tag) {
         __builtin_amdgcn_s_sleep(2);
@@ -207,6 +226,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     }
   }
   const int m0 = m_tile * TM, nb_base = n_tile * (NBW * WN) + wn * NBW;
+  uint32_t early[4];
+  ec_flags_early<TM, FUSED>(a, m0, early);
 
   // ---- X tile copies for step kc into stage st, through a buffer resource
   // over X: rows >= M fall outside it and units at k >= K are sent outside
@@ -407,7 +428,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   float* gs = reinterpret_cast<float*>(lds + ec_gs_offset<TM, TN>());
   bool any_gate = false;
   if (jblocks > 0) {
-    ec_prepare<TM, FUSED>(a, m0, tag, gs);
+    ec_prepare<TM, FUSED>(a, m0, tag, gs, early);
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) any_gate |= gs[wm * MBW * 16 + mb * 16 + c16] != 0.0f;
     any_gate = __any(any_gate);
