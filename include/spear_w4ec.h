@@ -126,10 +126,12 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
  * shape for a call (SPEAR page, abstract: the fusion variant adapts to the call).
  * Host only; touches the device only to read its CU count when
  * desc->device_cus == 0 (cached per device).
- * Rules: rank 0 or variant NO_EC -> NO_EC; AUTO -> FUSED when M is at most
- * the skinny-kernel limit (16 rows) and rank % 4 == 0, else SPLIT.  FUSED
- * outside those limits, and the tiled kernel (M > 16) with X or the packed
- * weight above 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value
+ * Rules: rank 0 or variant NO_EC -> NO_EC; AUTO -> FUSED when rank % 4 == 0
+ * (any M: the skinny kernel up to 16 rows, the tiled kernel above, both with
+ * the EC projection in the same launch), else SPLIT.  FUSED with
+ * rank % 4 != 0 (or with more than 4096 row tiles of 64 in the tiled case),
+ * and the tiled kernel (M > 16) with X or the packed weight above
+ * 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value
  * decision (skip the EC term of a tile whose gates are all below tau) is
  * taken on the device inside the epilogue, so no gate value ever crosses to
  * the host.
@@ -154,8 +156,9 @@ spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t
  *            before its first use.  Its first 256 KiB are a header owned by
  *            the library: cross-workgroup counters, which every call returns
  *            to zero, a call epoch, which every fused call advances by one,
- *            and the fused variant's hand-off slabs, whose entries carry the
- *            epoch of the call that wrote them.  The rest is scratch.  So a
+ *            and the fused variants' ready flags and hand-off slabs, which
+ *            carry the epoch of the call that wrote them.  The rest is
+ *            scratch.  So a
  *            zero-filled workspace can be reused, without clearing, by later
  *            calls of any plan that fit in it; the caller must not write to
  *            it between calls.  Calls that run concurrently must not share a
