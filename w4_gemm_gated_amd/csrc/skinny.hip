@@ -82,18 +82,21 @@ __device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
 // ---------------------------------------------------------------- producer
 //
 // Producer p owns the K slab [k0, k0 + ksp).  LDS: the A slab As[ksp][rank]
-// copied verbatim, the w_g slab Wh[ksp], the gate column Wg[ksp][4] (w_g in
-// column 0, zeros beside it), and the X slab Xs[16][ksp] whose 16-byte units
-// are XOR-swizzled by row (unit u of row r in slot u ^ (r % 16)), so the 16
-// rows of one fragment read hit 16 different bank groups.  B fragments of the
-// row-major A slab come from two transposing LDS reads (ds_read_b64_tr_b16):
-// within each 16-lane group, lane 4e + c supplies the address of
+// copied verbatim, the w_g slab Wh[ksp], one word that carries the call's
+// tag, and the X slab Xs[16][ksp] whose 16-byte units are XOR-swizzled by
+// row (unit u of row r in slot u ^ (r % 16)), so the 16 rows of one fragment
+// read hit 16 different bank groups.  B fragments of the row-major A slab
+// come from two transposing LDS reads (ds_read_b64_tr_b16): within each
+// 16-lane group, lane 4e + c supplies the address of
 // A[k + e][j + 4c .. j + 4c + 3], and lane i then holds A[k .. k + 3][j + i].
-// The gate block reads Wg the same way with row stride 4: its column 0 is
-// w_g, its other columns (finite neighbours) are never published.
+// The gate logit is one more matrix product whose B fragment is a plain
+// 16-byte read of Wh: every lane gets w_g at its own k, so all 16 columns of
+// that product hold the logit and only column 0 is published.
 
-constexpr int kPass = 4;                 // column blocks per pass
-constexpr int kRedBytes = 4 * kPass * kWave * 16;   // the four waves' sums of one pass
+constexpr int kPass = 4;                 // P column blocks per pass (the last pass adds the gate)
+constexpr int kCopyWaves = 3;            // waves that copy the slabs; the fourth warms the code
+constexpr int kRedSlots = kPass + 1;
+constexpr int kRedBytes = 4 * kRedSlots * kWave * 16;   // the four waves' sums of one pass
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
@@ -104,21 +107,21 @@ __host__ __device__ __forceinline__ int prod_a_units(int ksp, int rank) { return
 __host__ __device__ __forceinline__ int prod_w_units(int ksp) { return (ksp / 8 + kWave - 1) / kWave * kWave; }
 // The four waves' sums of a pass (red) overlay the X slab when there is one
 // pass only (the slab is no longer read then), else follow it.
-__host__ __device__ __forceinline__ bool producer_red_own(int rank) { return (rank + 15) / 16 + 1 > kPass; }
+__host__ __device__ __forceinline__ bool producer_red_own(int rank) { return (rank + 15) / 16 > kPass; }
 __host__ __device__ __forceinline__ size_t producer_xs_bytes(int ksp, int rank) {
   const size_t xs = (size_t)16 * ksp * 2;
   if (producer_red_own(rank)) return xs + kRedBytes;
   return xs > (size_t)kRedBytes ? xs : (size_t)kRedBytes;
 }
 __host__ __device__ __forceinline__ size_t producer_lds_bytes(int ksp, int rank) {
-  return (size_t)prod_a_units(ksp, rank) * 16 + 64 + (size_t)prod_w_units(ksp) * 16 + (size_t)ksp * 8 + 64 +
+  return (size_t)prod_a_units(ksp, rank) * 16 + 64 + (size_t)prod_w_units(ksp) * 16 + 16 +
          producer_xs_bytes(ksp, rank);
 }
 
 struct ProducerLds {
   half_t* As;
   half_t* Wh;
-  half_t* Wg;
+  uint32_t* tag;
   half_t* Xs;
 };
 
@@ -127,7 +130,7 @@ __device__ ProducerLds producer_lds(unsigned char* base, int ksp, int rank) {
   size_t off = 0;
   L.As = reinterpret_cast<half_t*>(base + off);  off += (size_t)prod_a_units(ksp, rank) * 16 + 64;
   L.Wh = reinterpret_cast<half_t*>(base + off);  off += (size_t)prod_w_units(ksp) * 16;
-  L.Wg = reinterpret_cast<half_t*>(base + off);  off += (size_t)ksp * 8 + 64;
+  L.tag = reinterpret_cast<uint32_t*>(base + off);  off += 16;
   L.Xs = reinterpret_cast<half_t*>(base + off);
   return L;
 }
@@ -142,105 +145,81 @@ __device__ __forceinline__ half8_t lds_b_fragment_tr(const half_t* row0, int ran
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
-  const int tid = threadIdx.x, lane = tid % kWave;
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+// ---- wave w takes the 32-k blocks kb = w, w + 4, ... of the slab (KBW
+// of them) for every P column block, kPass blocks a pass, and for the gate in
+// the last pass; the four waves' sums meet in LDS (red), and wave j stores
+// slot j (j + 4) of the pass.  Rows 4 t4 .. 4 t4 + 3 (< M) are published,
+// columns >= rank of a P block are not.  Nothing waits for the stores: the
+// tags tell the readers when they landed.
+//
+// The wave that copies nothing starts one pass early (nb0 = -kPass): it
+// reads the LDS while the copies are still landing and drops the sums.  Its
+// only purpose is to fetch the pass's instructions into the instruction
+// cache while the copies are in flight.  It has no loads of its own in
+// flight, so its LDS reads are not held back by the copies.
+template <int KBW>
+__device__ void producer_passes(const SkinnyKArgs& a, const ProducerLds& L, int p, int w, uint32_t tag) {
+  const int lane = threadIdx.x % kWave;
   const int c16 = lane % 16, t4 = lane / 16;
   const int ksp = a.ksp;
-  const int k0 = p * ksp;
-  const int kn = min(ksp, a.K - k0);          // multiple of 8
   const int pblocks = (a.rank + 15) / 16;
-  const int nblocks = pblocks + 1;            // the last block carries the gate logit
-  const ProducerLds L = producer_lds(lds, ksp, a.rank);
-  const uint32_t tag = ld_dev_u32(&a.sync[kEpoch]) + 1u;   // needed only at the end
-
-  // ---- slab copies, split over the four waves.  A slab rows k0 .. k0+kn
-  // (kn*rank/8 16-byte units; A is 16-byte aligned and k0*rank*2 is a
-  // multiple of 16) and the w_g slab; clamped units duplicate the last real
-  // unit.  X rows >= M and k >= K read as zeros.
-  {
-    const int nvec = kn * a.rank / 8;
-    const u32x4_t* asrc = reinterpret_cast<const u32x4_t*>(a.A + (size_t)k0 * a.rank);
-    for (int base = w * kWave; base < prod_a_units(ksp, a.rank); base += 4 * kWave)
-      copy_to_lds_16b(asrc + min(base + lane, nvec - 1), L.As + (size_t)base * 8);
-    const u32x4_t* wsrc = reinterpret_cast<const u32x4_t*>(a.w_g + k0);
-    for (int base = w * kWave; base < prod_w_units(ksp); base += 4 * kWave)
-      copy_to_lds_16b(wsrc + min(base + lane, kn / 8 - 1), L.Wh + (size_t)base * 8);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
-    const int units = ksp / 8;                 // per row, >= 16
-    for (int idx = w * kWave; idx < 16 * units; idx += 4 * kWave) {
-      const int row = (idx + lane) / units, slot = (idx + lane) % units;
-      const int unit = slot ^ (row % 16);
-      const int k = k0 + unit * 8;
-      const uint32_t voff = (row < a.M && k < a.K) ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)k) * 2u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(L.Xs + (size_t)idx * 8), 16, voff, 0, 0, 0);
-    }
-  }
-  drain_vm();
-  __syncthreads();
-
-  // ---- gate column: Wg[k][0] = w_g[k0 + k], Wg[k][1..3] = 0 (and slack rows)
-  for (int k = tid; k < ksp + 8; k += kThreads) {
-    const half_t wv = k < ksp ? L.Wh[k] : (half_t)0.0f;
-    half4_t q = {wv, (half_t)0.0f, (half_t)0.0f, (half_t)0.0f};
-    *reinterpret_cast<half4_t*>(L.Wg + (size_t)k * 4) = q;
-  }
-  __syncthreads();
-
-  // ---- wave w takes the 32-k blocks kb = w, w + 4, ... of the slab for
-  // every column block (P blocks, then the gate block), in passes of kPass
-  // blocks; the four waves' sums meet in LDS (red), and wave j stores block j
-  // of the pass.  Rows 4 t4 ..
-  // 4 t4 + 3 (< M) are published, columns >= rank of a P block are not.
-  // Nothing waits for the stores: the tags tell the readers when they landed.
   uint64_t* slab = a.handoff + (size_t)p * a.M * a.r1p;
-  const int kbw = ksp / 32 / 4;                // 32-k blocks per wave
   const half_t* xrow = L.Xs + (size_t)c16 * ksp;
   float4_t* red = reinterpret_cast<float4_t*>(L.Xs + (producer_red_own(a.rank) ? (size_t)16 * ksp : 0));
-                                               // [4 waves][kPass][64 lanes]
-  for (int nb0 = 0; nb0 < nblocks; nb0 += kPass) {
-    const half_t* bsrc[kPass];
-    int bstride[kPass];
-#pragma unroll
-    for (int j = 0; j < kPass; ++j) {
-      const int blk = min(nb0 + j, nblocks - 1);   // past the last: computed, never stored
-      const bool gate = blk == pblocks;
-      bsrc[j] = gate ? L.Wg : L.As + blk * 16;
-      bstride[j] = gate ? 4 : a.rank;
+                                               // [4 waves][kRedSlots][64 lanes]
+#pragma clang loop unroll(disable)
+  for (int nb0 = w < kCopyWaves ? 0 : -kPass; nb0 < pblocks; nb0 += kPass) {
+    if (nb0 == 0) {
+      drain_vm();
+      if (w == 0 && lane == 0) *L.tag = tag;
+      __syncthreads();
+      tag = __builtin_amdgcn_readfirstlane(*L.tag);
     }
-    float4_t acc[kPass];
+    const int nbp = max(nb0, 0);
+    const int np = min(kPass, pblocks - nbp);  // P blocks of this pass
+    const bool last = nbp + kPass >= pblocks;  // the gate rides on the last pass
+    float4_t acc[kPass], accg = zero_float4();
 #pragma unroll
     for (int j = 0; j < kPass; ++j) acc[j] = zero_float4();
-    // Every LDS fragment read of the pass is issued before the first matrix
-    // instruction (kbw <= 8: ksp <= 1024; reads past kbw repeat the last
-    // block and are not used).
-    constexpr int kMaxKbw = 8;
-    half8_t xf[kMaxKbw], bf[kMaxKbw][kPass];
+    // The k-blocks go in groups of up to four: every LDS fragment read of a
+    // group is issued before its first matrix instruction.  P blocks past np
+    // are neither read nor multiplied.
+    constexpr int kGroup = KBW < 4 ? KBW : 4;
 #pragma unroll
-    for (int i = 0; i < kMaxKbw; ++i) {
-      const int kb = w + 4 * min(i, kbw - 1);
-      xf[i] = *reinterpret_cast<const half8_t*>(xrow + (size_t)(((kb * 4 + t4) ^ c16) * 8));
+    for (int i0 = 0; i0 < KBW; i0 += kGroup) {
+      half8_t xf[kGroup], gf[kGroup], bf[kGroup][kPass];
 #pragma unroll
-      for (int j = 0; j < kPass; ++j)
-        bf[i][j] = lds_b_fragment_tr(bsrc[j] + (size_t)kb * 32 * bstride[j], bstride[j], lane);
-    }
+      for (int i = 0; i < kGroup; ++i) {
+        const int kb = w + 4 * (i0 + i);
+        xf[i] = *reinterpret_cast<const half8_t*>(xrow + (size_t)(((kb * 4 + t4) ^ c16) * 8));
+        gf[i] = *reinterpret_cast<const half8_t*>(L.Wh + (size_t)kb * 32 + 8 * t4);
 #pragma unroll
-    for (int i = 0; i < kMaxKbw; ++i)
-      if (i < kbw) {
-#pragma unroll
-        for (int j = 0; j < kPass; ++j) acc[j] = mfma16x16x32(xf[i], bf[i][j], acc[j]);
+        for (int j = 0; j < kPass; ++j)
+          if (j < np)
+            bf[i][j] = lds_b_fragment_tr(L.As + (size_t)(nbp + j) * 16 + (size_t)kb * 32 * a.rank, a.rank, lane);
       }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+#pragma unroll
+        for (int j = 0; j < kPass; ++j)
+          if (j < np) acc[j] = mfma16x16x32(xf[i], bf[i][j], acc[j]);
+        accg = mfma16x16x32(xf[i], gf[i], accg);
+      }
+    }
+    if (nb0 < 0) continue;
     __syncthreads();                           // every wave is done with the X slab / last pass
 #pragma unroll
-    for (int j = 0; j < kPass; ++j) red[(w * kPass + j) * kWave + lane] = acc[j];
+    for (int j = 0; j < kPass; ++j) red[(w * kRedSlots + j) * kWave + lane] = acc[j];
+    red[(w * kRedSlots + kPass) * kWave + lane] = accg;
     __syncthreads();
-    const int blk = nb0 + w;
-    if (w < kPass && blk < nblocks) {
-      float4_t sum = red[(0 * kPass + w) * kWave + lane];
+    const int nslots = np + (last ? 1 : 0);
+    for (int sl = w; sl < nslots; sl += 4) {
+      const bool gate = sl == np;
+      const int rs = gate ? kPass : sl;
+      float4_t sum = red[(0 * kRedSlots + rs) * kWave + lane];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) sum += red[(q * kPass + w) * kWave + lane];
-      const bool gate = blk == pblocks;
-      const int col = gate ? a.rank : blk * 16 + c16;
+      for (int q = 1; q < 4; ++q) sum += red[(q * kRedSlots + rs) * kWave + lane];
+      const int col = gate ? a.rank : (nbp + sl) * 16 + c16;
       if (gate ? c16 == 0 : col < a.rank) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
@@ -251,6 +230,46 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
   }
 }
 
+__device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ksp = a.ksp;                      // 128, 256, 512 or 1024
+  const int k0 = p * ksp;
+  const int kn = min(ksp, a.K - k0);          // multiple of 8
+  const ProducerLds L = producer_lds(lds, ksp, a.rank);
+  uint32_t tag = 0;                           // needed only at the end
+
+  // ---- slab copies, split over waves 0 .. kCopyWaves-1.  A slab rows
+  // k0 .. k0+kn (kn*rank/8 16-byte units; A is 16-byte aligned and
+  // k0*rank*2 is a multiple of 16) and the w_g slab; clamped units duplicate
+  // the last real unit.  X rows >= M and k >= K read as zeros.
+  if (w < kCopyWaves) {
+    if (w == 0) tag = ld_dev_u32(&a.sync[kEpoch]) + 1u;
+    const int nvec = kn * a.rank / 8;
+    const u32x4_t* asrc = reinterpret_cast<const u32x4_t*>(a.A + (size_t)k0 * a.rank);
+    for (int base = w * kWave; base < prod_a_units(ksp, a.rank); base += kCopyWaves * kWave)
+      copy_to_lds_16b(asrc + min(base + lane, nvec - 1), L.As + (size_t)base * 8);
+    const u32x4_t* wsrc = reinterpret_cast<const u32x4_t*>(a.w_g + k0);
+    for (int base = w * kWave; base < prod_w_units(ksp); base += kCopyWaves * kWave)
+      copy_to_lds_16b(wsrc + min(base + lane, kn / 8 - 1), L.Wh + (size_t)base * 8);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
+    const int units = ksp / 8;                 // per row, >= 16
+    for (int idx = w * kWave; idx < 16 * units; idx += kCopyWaves * kWave) {
+      const int row = (idx + lane) / units, slot = (idx + lane) % units;
+      const int unit = slot ^ (row % 16);
+      const int k = k0 + unit * 8;
+      const uint32_t voff = (row < a.M && k < a.K) ? ((uint32_t)row * (uint32_t)a.K + (uint32_t)k) * 2u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(L.Xs + (size_t)idx * 8), 16, voff, 0, 0, 0);
+    }
+  }
+
+  const int kbw = ksp / 32 / 4;                // 32-k blocks per wave: 1, 2, 4 or 8
+  if (kbw == 1) producer_passes<1>(a, L, p, w, tag);
+  else if (kbw == 2) producer_passes<2>(a, L, p, w, tag);
+  else if (kbw == 4) producer_passes<4>(a, L, p, w, tag);
+  else producer_passes<8>(a, L, p, w, tag);
+}
+
 // ---------------------------------------------------------------- GEMM tile
 
 // Static LDS of a GEMM workgroup: the sums of waves 1..3, then flags and the
@@ -258,8 +277,10 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
 constexpr size_t static_lds_bytes(int nbw) { return (size_t)3 * kWave * nbw * 16 + 512; }
 
 // Dynamic LDS of a GEMM workgroup with the EC on: the EC factor tile
-// Bs[jblocks*32][TN] (fp16); Pc[16][rank + 1] floats (P, then the final gate
-// g'); then, split variant, Pt[16][ps] floats and gt[16].
+// Bs[jblocks*32][TN] (fp16); Pc[16][pcs] floats (P in columns < rank, the
+// final gate g' in column rank; pcs keeps every row 16-byte aligned and at
+// least ps wide, so a row's P fragment is two 16-byte reads); then, split
+// variant, Pt[16][ps] floats and gt[16].
 //
 // The EC operands that are ready at the start (the B tile, the split
 // variant's P and g) are loaded into registers ahead of the weight stream, a
@@ -273,7 +294,11 @@ constexpr int kPLoads = 1;    // split: 16-byte units of P per thread
 __host__ __device__ __forceinline__ size_t gemm_bs_bytes(int ps, int tn) {
   return ((size_t)ps * tn * 2 + 15) & ~(size_t)15;
 }
-__host__ __device__ __forceinline__ size_t gemm_pc_bytes(int rank) { return ((size_t)16 * (rank + 1) * 4 + 15) & ~(size_t)15; }
+__host__ __device__ __forceinline__ int gemm_pc_stride(int rank, int ps) {
+  const int w = rank + 1 > ps ? rank + 1 : ps;
+  return (w + 3) & ~3;
+}
+__host__ __device__ __forceinline__ size_t gemm_pc_bytes(int rank, int ps) { return (size_t)16 * gemm_pc_stride(rank, ps) * 4; }
 __host__ __device__ __forceinline__ size_t gemm_table_bytes(int ec_mode, int ps, int r1p, int P, int M) {
   if (ec_mode == 1) return 0;   // the fused hand-off is summed in registers
   return (size_t)16 * ps * 4 + 16 * 4;
@@ -282,56 +307,58 @@ __host__ __device__ __forceinline__ size_t gemm_table_bytes(int ec_mode, int ps,
 // Fused consumer: the final [P | g'] of this call from the producers' slabs.
 // Thread t takes 16-byte units q = t, t + 256, ... of a slab (two entries of
 // row q / (r1p / 2)) and loads that unit of every slab, Q units x PB slabs
-// in flight at once (one memory round trip per batch); units whose tag is
-// not yet this call's are reloaded (bounded wait).  The slabs are added in
-// fixed order and the gate applied to column rank.
+// in flight at once (one memory round trip per batch).  While any lane of the
+// wave holds a unit whose tag is not yet this call's, the wave reloads the
+// whole batch (bounded wait).  The code has no per-unit branches: offsets of
+// absent units are out of range (they read as zeros) and the tag test is
+// plain arithmetic.  The slabs are added in fixed order and the gate applied
+// to column rank; the result goes to Pc[row][col] (row stride pcs).
 template <int Q, int PB>
-__device__ void gather_handoff(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, uint32_t tag, float* Pc) {
+__device__ void gather_handoff(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, uint32_t tag, float* Pc, int pcs) {
   const int tid = threadIdx.x;
   const int r1 = a.rank + 1;
   const int pairs = a.M * a.r1p / 2;                     // 16-byte units per slab
   const uint32_t slab_bytes = (uint32_t)a.M * (uint32_t)a.r1p * 8u;
   for (int q0 = 0; q0 < pairs; q0 += Q * kThreads) {
     float s0[Q], s1[Q];
+    uint32_t off[Q];
+    bool two[Q];                                         // entry 1 is a real column
 #pragma unroll
-    for (int i = 0; i < Q; ++i) s0[i] = s1[i] = 0.0f;
+    for (int i = 0; i < Q; ++i) {
+      const int q = q0 + i * kThreads + tid;
+      s0[i] = s1[i] = 0.0f;
+      off[i] = q < pairs ? (uint32_t)q * 16u : kOutOfRange;
+      two[i] = (2 * q) % a.r1p + 1 < r1;
+    }
     for (int p0 = 0; p0 < a.P; p0 += PB) {
       u32x4_t v[Q][PB];
-      auto offset = [&](int i, int j) -> uint32_t {
-        const int q = q0 + i * kThreads + tid;
-        return (q < pairs && p0 + j < a.P) ? (uint32_t)(p0 + j) * slab_bytes + (uint32_t)q * 16u : kOutOfRange;
-      };
-      // Entry 1 of a unit past column rank is never written (tag 0).
-      auto ready = [&](int i, const u32x4_t& u) -> bool {
-        const int c0 = (2 * (q0 + i * kThreads + tid)) % a.r1p;
-        return u[1] == tag && (c0 + 1 >= r1 || u[3] == tag);
-      };
+      auto issue = [&]() {
 #pragma unroll
-      for (int i = 0; i < Q; ++i)
+        for (int i = 0; i < Q; ++i)
 #pragma unroll
-        for (int j = 0; j < PB; ++j)
-          v[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, offset(i, j), 0,
-                                                                                        kCachePolicySc1));
-      uint32_t n = 0;
-      for (;;) {
+          for (int j = 0; j < PB; ++j) {
+            // off + slab offset stays out of range when off is (no wrap).
+            const uint32_t o = p0 + j < a.P ? off[i] + (uint32_t)(p0 + j) * slab_bytes : kOutOfRange;
+            v[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, o, 0, kCachePolicySc1));
+          }
+      };
+      issue();
+      for (uint32_t n = 0;; ++n) {
         bool stale = false;
 #pragma unroll
         for (int i = 0; i < Q; ++i)
 #pragma unroll
-          for (int j = 0; j < PB; ++j) stale |= offset(i, j) != kOutOfRange && !ready(i, v[i][j]);
-        if (!stale) break;
-        if (++n > a.spin_limit) {
-          st_dev_u32(&a.sync[kError], 1u);
+          for (int j = 0; j < PB; ++j) {
+            const bool ready = (v[i][j][1] == tag) & (!two[i] | (v[i][j][3] == tag));
+            stale |= (p0 + j < a.P) & (off[i] != kOutOfRange) & !ready;
+          }
+        if (!__any(stale)) break;
+        if (n >= a.spin_limit) {
+          if (tid % kWave == 0) st_dev_u32(&a.sync[kError], 1u);
           break;
         }
         __builtin_amdgcn_s_sleep(4);
-#pragma unroll
-        for (int i = 0; i < Q; ++i)
-#pragma unroll
-          for (int j = 0; j < PB; ++j)
-            if (offset(i, j) != kOutOfRange && !ready(i, v[i][j]))
-              v[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, offset(i, j), 0,
-                                                                                            kCachePolicySc1));
+        issue();
       }
 #pragma unroll
       for (int i = 0; i < Q; ++i)
@@ -356,7 +383,7 @@ __device__ void gather_handoff(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, 
           v = sigmoidf_(v + a.gate_bias);
           if (a.skip_tau > 0.0f && !(v >= a.skip_tau)) v = 0.0f;
         }
-        Pc[row * r1 + col] = v;
+        Pc[row * pcs + col] = v;
       }
     }
   }
@@ -385,10 +412,10 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
   const int nb0 = t * NBW;
   const int n0 = nb0 * 16;
   const int jblocks = ECM ? a.ps / 32 : 0;
-  const int r1 = a.rank + 1;
   half_t* Bs = reinterpret_cast<half_t*>(dyn_lds);
   float* Pc = reinterpret_cast<float*>(dyn_lds + gemm_bs_bytes(a.ps, TN));
-  unsigned char* table = dyn_lds + gemm_bs_bytes(a.ps, TN) + gemm_pc_bytes(a.rank);
+  unsigned char* table = dyn_lds + gemm_bs_bytes(a.ps, TN) + gemm_pc_bytes(a.rank, a.ps);
+  const int pcs = gemm_pc_stride(a.rank, a.ps);
   // The epoch is read before the weight stream is requested, so it returns
   // ahead of it.
   const uint32_t tag = ECM == 1 ? ld_dev_u32(&a.sync[kEpoch]) + 1u : 0u;
@@ -557,8 +584,8 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
     // earlier, the loads would queue behind the weight stream and be served
     // about when it is, normally just before the producers publish, which
     // costs a second round trip.)  Sixteen loads in flight per thread.
-    if (a.P <= 8) gather_handoff<2, 8>(a, hr, tag, Pc);
-    else gather_handoff<1, 16>(a, hr, tag, Pc);
+    if (a.P <= 8) gather_handoff<2, 8>(a, hr, tag, Pc, pcs);
+    else gather_handoff<1, 16>(a, hr, tag, Pc, pcs);
     __syncthreads();
     // Count this workgroup out (wave 1, off wave 0's path): the last one
     // returns the counters to zero and advances the epoch (every producer and
@@ -573,33 +600,31 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
   }
   if (w > 0) return;
 
-  // ---- gated EC epilogue (wave 0)
-  auto ec_value = [&](int row, int col) -> float {   // P (col < rank) or g (col == rank)
-    if (ECM == 1) return Pc[row * r1 + col];
-    const float* Pt = reinterpret_cast<const float*>(table);
-    if (col < a.rank) return Pt[row * a.ps + col];
-    return reinterpret_cast<const float*>(table + (size_t)16 * a.ps * 4)[row];
-  };
+  // ---- gated EC epilogue (wave 0).  Lane (t4, c16): P row c16, columns
+  // 8 t4 .. 8 t4 + 7 of each 32-column block (two 16-byte reads of a
+  // 16-byte aligned row), times the row's gate, as the A fragment; the B
+  // fragment of Bs from two transposing reads.
+  const float* prow = ECM == 1 ? Pc + (size_t)c16 * pcs : reinterpret_cast<const float*>(table) + (size_t)c16 * a.ps;
   float4_t ec[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) ec[nb] = zero_float4();
   if (ECM) {
-    const float gv = c16 < a.M ? ec_value(c16, a.rank) : 0.0f;   // the final gate g'
+    const float gv = c16 < a.M ? (ECM == 1 ? prow[a.rank] : reinterpret_cast<const float*>(table + (size_t)16 * a.ps * 4)[c16])
+                               : 0.0f;                   // the final gate g'
     if (__any(gv != 0.0f)) {
       for (int jb = 0; jb < jblocks; ++jb) {
+        const int k0 = jb * 32 + 8 * t4;
+        const float4_t lo = *reinterpret_cast<const float4_t*>(prow + k0);
+        const float4_t hi = *reinterpret_cast<const float4_t*>(prow + k0 + 4);
         half8_t pa;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int col = jb * 32 + 8 * t4 + e;
-          pa[e] = (col < a.rank && gv != 0.0f) ? (half_t)(gv * ec_value(c16, col)) : (half_t)0.0f;
+          const float pv = e < 4 ? lo[e] : hi[e - 4];
+          pa[e] = (k0 + e < a.rank && gv != 0.0f) ? (half_t)(gv * pv) : (half_t)0.0f;
         }
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          half8_t bb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bb[e] = Bs[(jb * 32 + 8 * t4 + e) * TN + nb * 16 + c16];
-          ec[nb] = mfma16x16x32(pa, bb, ec[nb]);
-        }
+        for (int nb = 0; nb < NBW; ++nb)
+          ec[nb] = mfma16x16x32(pa, lds_b_fragment_tr(Bs + (size_t)jb * 32 * TN + nb * 16, TN, lane), ec[nb]);
       }
     }
   }
@@ -711,7 +736,7 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
     sh.lds = producer_lds_bytes((int)ksp, (int)rank);
   }
   if (rank > 0)
-    sh.lds_gemm = gemm_bs_bytes(ps, sh.nbw * 16) + gemm_pc_bytes((int)rank) +
+    sh.lds_gemm = gemm_bs_bytes(ps, sh.nbw * 16) + gemm_pc_bytes((int)rank, ps) +
                   gemm_table_bytes(fused ? 1 : 2, ps, r1p, sh.P, (int)M);
   // Workspace: sync words in the counter header and the hand-off slabs in the
   // header's hand-off region; the split-K slots as scratch from scratch_base
