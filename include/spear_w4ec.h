@@ -87,7 +87,7 @@ typedef struct spear_plan {
   int32_t producers;      /* workgroups that compute the EC projection */
   int32_t ec_split;       /* K slices of the EC projection */
   int32_t cus;            /* compute units planned for */
-  int32_t reserved;
+  int32_t ec_local;       /* 1: every workgroup of the main launch computes the EC projection itself */
   size_t workspace_bytes; /* device workspace the call needs (0 = none) */
 } spear_plan_t;
 
@@ -128,7 +128,12 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
  * desc->device_cus == 0 (cached per device).
  * Rules: rank 0 or variant NO_EC -> NO_EC; AUTO -> FUSED when rank % 4 == 0
  * (any M: the skinny kernel up to 16 rows, the tiled kernel above, both with
- * the EC projection in the same launch), else SPLIT.  FUSED with
+ * the EC projection in the same launch), else SPLIT.  Skinny FUSED takes
+ * one of two forms, reported by plan.ec_local: when the weight GEMM needs no
+ * K split, rank <= 64 and A is at most 128 KiB, every GEMM workgroup
+ * computes the whole projection itself with four extra waves (ec_local = 1,
+ * producers = 0, no workspace); otherwise producer workgroups lead the grid
+ * and hand P and the gate over through the workspace (ec_local = 0).  FUSED with
  * rank % 4 != 0 (or with more than 4096 row tiles of 64 in the tiled case),
  * and the tiled kernel (M > 16) with X or the packed weight above
  * 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value

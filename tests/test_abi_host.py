@@ -66,7 +66,7 @@ def plan(lib, M, K, N, r, variant=0, cus=256, bias=0.0, tau=0.0):
 
 def test_dispatch_rules(lib):
     st, p = plan(lib, 16, 4096, 4096, 32)
-    assert st == 0 and p.variant in (1, 2) and p.kernel == 0 and p.workspace_bytes > 0
+    assert st == 0 and p.variant == 1 and p.kernel == 0
     # tiled fused: about 64 EC workgroups (32 row tiles x 2 K slices) lead
     # the grid, then the 8 x 64 tiles of 256 x 224
     st, p = plan(lib, 2048, 4096, 14336, 64)
@@ -79,9 +79,26 @@ def test_dispatch_rules(lib):
     st, p = plan(lib, 64, 14336, 4096, 64)
     assert st == 0 and p.variant == 1 and p.producers == 14 and p.grid == 16 + 32 * p.split_k
     st, p = plan(lib, 16, 4096, 4096, 32)
-    # fused: the EC producer workgroups, then the GEMM tiles (256 panels of
-    # 16 columns, one K range)
-    assert p.variant == 1 and p.producers == 8 and p.grid == 256 + 8 and p.split_k == 1
+    # fused, A of 256 KiB: the EC producer workgroups, then the GEMM tiles
+    # (256 panels of 16 columns, one K range); P goes over through the workspace
+    assert p.variant == 1 and p.ec_local == 0 and p.producers == 8 and p.grid == 256 + 8 and p.split_k == 1
+    assert p.workspace_bytes > 0
+    # fused, local EC: one K range and an A of at most 128 KiB, so every GEMM
+    # workgroup computes the projection itself; no producers, no workspace
+    st, p = plan(lib, 16, 2048, 4096, 32)
+    assert st == 0 and p.ec_local == 1 and p.producers == 0 and p.grid == 256 and p.workspace_bytes == 0
+    st, p = plan(lib, 1, 1024, 14336, 64)
+    assert st == 0 and p.ec_local == 1 and p.split_k == 1
+    st, p = plan(lib, 16, 4096, 14336, 64)
+    assert st == 0 and p.ec_local == 0 and p.producers > 0       # A of 512 KiB: hand-off
+    # fused with a K split: producer workgroups lead the grid
+    st, p = plan(lib, 1, 14336, 4096, 64)
+    assert st == 0 and p.variant == 1 and p.ec_local == 0 and p.split_k == 7 and p.producers == 56
+    assert p.grid == 56 + 64 * 7 and p.workspace_bytes > 0
+    st, p = plan(lib, 1, 8192, 4096, 64)
+    assert st == 0 and p.ec_local == 0 and p.producers > 0      # A of 1 MiB: hand-off
+    st, p = plan(lib, 16, 512, 512, 16)
+    assert st == 0 and p.ec_local == 0 and p.split_k > 1 and p.producers > 0
     st, p = plan(lib, 4, 4096, 4096, 30)
     assert st == 0 and p.variant == 2     # fused needs rank % 4 == 0: auto takes split
     st, p = plan(lib, 4, 4096, 4096, 30, variant=1)

@@ -178,12 +178,30 @@ def test_ragged_shapes(M, K, N, r):
 
 
 @pytest.mark.parametrize("M,K,N,r", [(3, 136, 20, 4), (16, 1000, 100, 20), (7, 264, 40, 36), (4, 512, 48, 256),
-                                     (1, 8, 1, 4), (16, 2056, 4096, 32)])
+                                     (1, 8, 1, 4), (16, 2056, 4096, 32), (2, 4104, 520, 64), (5, 8192, 256, 64),
+                                     (3, 4096, 1000, 68)])
 def test_fused_ragged_shapes(M, K, N, r):
     """The single-launch variant on K tails (K % 32 != 0), partial column
-    blocks of A (rank % 16 != 0), one-column outputs and the largest rank."""
+    blocks of A (rank % 16 != 0), one-column outputs and the largest rank;
+    both the local EC (one K range, small A) and the producers' hand-off (a
+    K split, rank above 64 or a large A)."""
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=3 * M + K + N + r, outliers=True)
+    p = sp.spear_dispatch_plan(M, K, N, r, -0.5, variant="fused")
+    note(f"fused ragged M={M} K={K} N={N} r={r}: ec_local={p.ec_local} producers={p.producers} split_k={p.split_k}")
     layer_case(X, W, A, B, w_g, -0.5, 0.0, "fused", f"fused ragged M={M} K={K} N={N} r={r}")
+
+
+@pytest.mark.parametrize("M,K,N,r", [(3, 1000, 4096, 20), (7, 264, 4096, 36), (2, 520, 4096, 4),
+                                     (5, 1032, 6000, 52), (16, 1024, 14336, 64), (16, 2048, 4096, 32)])
+def test_local_ec_ragged_shapes(M, K, N, r):
+    """The fused skinny launch with the local EC (every workgroup computes the
+    projection itself): K tails inside the last chunk of A, partial column
+    blocks of A, the two chunk shapes (rank <= 32 and <= 64), a partial last
+    column panel and the largest A the planner keeps local (128 KiB)."""
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=13 * M + K + N + r, outliers=True)
+    p = sp.spear_dispatch_plan(M, K, N, r, 0.4, variant="fused")
+    assert p.ec_local == 1 and p.producers == 0
+    layer_case(X, W, A, B, w_g, 0.4, 0.0, "fused", f"local EC M={M} K={K} N={N} r={r}")
 
 
 @pytest.mark.parametrize("variant", ["fused", "split"])
@@ -241,23 +259,47 @@ def test_gate_zero_matches_no_ec_bitwise():
     assert np.array_equal(Y_off.astype(np.float64), Y_noec.astype(np.float64))
 
 
-def test_repeat_calls_deterministic_and_workspace_clean():
-    w = workloads.workload(2)
-    Wq_d, s_d = sp.spear_pack_w4(cuda(w["W"]))
-    p = sp.spear_dispatch_plan(16, 4096, 4096, 32, -1.0)
-    ws = torch.zeros(p.workspace_bytes, dtype=torch.uint8, device=DEV)
-    args = (cuda(w["X"]), Wq_d, s_d, cuda(w["A"]), cuda(w["B"]), cuda(w["w_g"]), -1.0)
-    Y1 = sp.spear_w4ec_linear(*args, plan=p, workspace=ws).clone()
-    Y2 = sp.spear_w4ec_linear(*args, plan=p, workspace=ws).clone()
+def test_local_ec_repeat_calls():
+    """A decode shape with a small A: every GEMM workgroup computes the EC
+    projection itself (no producers, no workspace); two calls give identical
+    results."""
+    M, K, N, r = 16, 2048, 4096, 32
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=19, outliers=True)
+    Wq_d, s_d = sp.spear_pack_w4(cuda(W))
+    p = sp.spear_dispatch_plan(M, K, N, r, -1.0)
+    assert p.variant == 1 and p.ec_local == 1 and p.producers == 0 and p.workspace_bytes == 0
+    args = (cuda(X), Wq_d, s_d, cuda(A), cuda(B), cuda(w_g), -1.0)
+    Y1 = sp.spear_w4ec_linear(*args, N=N, plan=p).clone()
+    Y2 = sp.spear_w4ec_linear(*args, N=N, plan=p).clone()
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
-    # the counters of the header are back at zero, and the call epoch (word 96
-    # of the GEMM counter region at 32 KiB) counts the two fused calls
+    Wq_o, s_o = oracle.pack_w4(W)
+    compare(Y1.cpu().numpy(), X, Wq_o, s_o, A, B, w_g, -1.0, 0.0, K, N, "local EC repeat")
+
+
+def test_handoff_repeat_calls_and_workspace_clean():
+    """A decode shape with a K split takes the producers' hand-off: two calls
+    on one workspace give identical results, the counters of the header are
+    back at zero and the call epoch (word 96 of the GEMM counter region at
+    32 KiB) counts the two calls."""
+    M, K, N, r = 2, 8192, 1024, 64
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=17, outliers=True)
+    Wq_d, s_d = sp.spear_pack_w4(cuda(W))
+    p = sp.spear_dispatch_plan(M, K, N, r, -1.0)
+    assert p.variant == 1 and p.ec_local == 0 and p.producers > 0
+    ws = torch.zeros(p.workspace_bytes, dtype=torch.uint8, device=DEV)
+    args = (cuda(X), Wq_d, s_d, cuda(A), cuda(B), cuda(w_g), -1.0)
+    Y1 = sp.spear_w4ec_linear(*args, N=N, plan=p, workspace=ws).clone()
+    Y2 = sp.spear_w4ec_linear(*args, N=N, plan=p, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
     counters = ws[: 64 * 1024].view(torch.int32).clone()
     epoch_word = 32 * 1024 // 4 + 96
     assert int(counters[epoch_word].item()) == 2
     counters[epoch_word] = 0
     assert int(counters.abs().sum().item()) == 0
+    Wq_o, s_o = oracle.pack_w4(W)
+    compare(Y1.cpu().numpy(), X, Wq_o, s_o, A, B, w_g, -1.0, 0.0, K, N, "hand-off repeat")
 
 
 def test_tiled_fused_repeat_calls_and_workspace():

@@ -55,7 +55,7 @@ class Plan(ctypes.Structure):
         ("M", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32), ("rank", ctypes.c_int32),
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("split_k", ctypes.c_int32),
         ("grid", ctypes.c_int32), ("producers", ctypes.c_int32), ("ec_split", ctypes.c_int32),
-        ("cus", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("cus", ctypes.c_int32), ("ec_local", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

@@ -114,7 +114,8 @@ struct SkinnyShape {
   int T = 0;        // column tiles
   int CPS = 0;      // 128-k chunks per split
   int CPW = 1;      // chunks per wave (<= 4)
-  int P = 0;        // EC producer workgroups (fused variant)
+  bool local_ec = false;  // fused: every GEMM workgroup computes the projection itself
+  int P = 0;        // EC producer workgroups (fused variant, hand-off)
   int ksp = 0;      // k per producer slab
   size_t lds = 0;   // dynamic LDS of a producer
   size_t lds_gemm = 0;  // dynamic LDS of a GEMM workgroup (EC factor tile)
@@ -136,7 +137,7 @@ struct SkinnyLaunch {
   const void* w_g;
   void* Y;
   int32_t M, K, N, rank;
-  int32_t ec_mode;          // 0 none, 1 fused, 2 P/g given
+  int32_t ec_mode;          // 0 none, 1 fused (hand-off or local, per shape), 2 P/g given
   float gate_bias, skip_tau;
   void* workspace;          // skinny workspace (layout in shape)
   const float* Pext;        // ec_mode 2

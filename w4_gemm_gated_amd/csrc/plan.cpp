@@ -87,6 +87,7 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     if (p.variant == SPEAR_VARIANT_FUSED) {
       p.producers = sh.P;
       p.ec_split = sh.P;
+      p.ec_local = sh.local_ec ? 1 : 0;
     }
     if (sh.ws_bytes > ws) ws = sh.ws_bytes;
   } else {

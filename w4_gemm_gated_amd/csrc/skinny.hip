@@ -270,6 +270,113 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
   else producer_passes<8>(a, L, p, w, tag);
 }
 
+// ---------------------------------------------------------------- local EC
+//
+// ec_mode 3: every GEMM workgroup computes the whole [P | z] = X [A | w_g]
+// itself, with four more waves (the local waves) that run while its four
+// weight waves stream W; no other workgroup is involved and nothing crosses
+// workgroups.  A is read by every workgroup, so it is served from L2 after
+// the first touch on each XCD; the planner takes this mode only for small A.
+// Local wave lw takes a contiguous range of chunks of A (8 KiB each: 128
+// rows up to rank 32, 64 rows up to rank 64).  A chunk's
+// rows (16-byte units, as they are in memory) go through registers into the
+// wave's own LDS buffer and come back as B fragments from transposing reads;
+// the X fragments and the gate fragments (plain 16-byte reads of w_g, as in
+// the producer) come straight from memory.  The next chunk's loads are in
+// flight while a chunk is multiplied.  The four waves' sums go to LDS (part)
+// for wave 0, which adds them in fixed order after the block's barrier.
+
+constexpr int kLocalWaves = 4;
+constexpr int kLocalSlots = 5;       // P column blocks (up to four), then the gate
+// A read by every workgroup (from L2).  Measured crossover against the
+// hand-off on a 4096-column decode: local wins by 2.3-2.5 us at 64 KiB of A,
+// slightly at 128 KiB, and loses by 2.6-3.2 us at 256 KiB.
+constexpr size_t kLocalMaxABytes = 128 * 1024;
+constexpr size_t kLocalBufBytes = 8 * 1024;      // one chunk: 8 units of 16 bytes per lane
+__host__ __device__ __forceinline__ int local_pb(int rank) { return rank <= 32 ? 2 : 4; }
+__host__ __device__ __forceinline__ size_t local_buf_bytes(int) { return kLocalBufBytes; }
+__host__ __device__ __forceinline__ size_t local_lds_bytes(int rank) {
+  return kLocalWaves * local_buf_bytes(rank) + (size_t)kLocalWaves * kLocalSlots * kWave * 16;
+}
+
+// PB column blocks (rank <= 16 PB); a chunk holds KB = 8 / PB 32-row blocks.
+template <int PB>
+struct LocalChunk {
+  static constexpr int KB = 8 / PB;
+  u32x4_t a[8];        // A units i * 64 + lane of the chunk
+  half8_t x[KB];       // X fragments of the chunk's 32-k blocks
+  half8_t g[KB];       // gate fragments (w_g) of the same blocks
+};
+
+template <int PB>
+__device__ void ec_local_pass(const SkinnyKArgs& a, unsigned char* base, int lw) {
+  const int lane = threadIdx.x % kWave, c16 = lane % 16, t4 = lane / 16;
+  half_t* buf = reinterpret_cast<half_t*>(base + (size_t)lw * local_buf_bytes(a.rank));
+  float4_t* part = reinterpret_cast<float4_t*>(base + kLocalWaves * local_buf_bytes(a.rank));
+  constexpr int KB = LocalChunk<PB>::KB, kRows = 32 * KB;
+  const int pblocks = (a.rank + 15) / 16;
+  const int nch = (a.K + kRows - 1) / kRows;
+  const int ch0 = lw * nch / kLocalWaves, ch1 = (lw + 1) * nch / kLocalWaves;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.w_g, (uint32_t)a.K * 2u);
+  const uint32_t xrow_off = c16 < a.M ? (uint32_t)c16 * (uint32_t)a.K * 2u : kOutOfRange;
+  const u32x4_t* A16 = reinterpret_cast<const u32x4_t*>(a.A);
+  // Rows past K: units clamped to the chunk's last real unit (finite), and
+  // their X and w_g read as zeros.
+  auto load = [&](LocalChunk<PB>& c, int ch) {
+    const int r0 = ch * kRows;
+    const int nvalid = min(kRows, a.K - r0) * a.rank / 8;   // rank % 4 == 0, K % 8 == 0
+    const size_t u0 = (size_t)r0 * a.rank / 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c.a[i] = A16[u0 + min(i * kWave + lane, nvalid - 1)];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int k = r0 + 32 * j + 8 * t4;
+      c.x[j] = buffer_load_half8(xr, k < a.K ? xrow_off + 2u * (uint32_t)k : kOutOfRange);
+      c.g[j] = buffer_load_half8(gr, k < a.K ? 2u * (uint32_t)k : kOutOfRange);
+    }
+  };
+  float4_t acc[PB], accg = zero_float4();
+#pragma unroll
+  for (int p = 0; p < PB; ++p) acc[p] = zero_float4();
+  auto process = [&](const LocalChunk<PB>& c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(buf + (size_t)(i * kWave + lane) * 8) = c.a[i];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+        if (p < pblocks)
+          acc[p] = mfma16x16x32(c.x[j], lds_b_fragment_tr(buf + (size_t)j * 32 * a.rank + p * 16, a.rank, lane), acc[p]);
+      accg = mfma16x16x32(c.x[j], c.g[j], accg);
+    }
+  };
+  // Two chunks in registers: the steady-state loop issues every load
+  // unconditionally, so the compiler's wait before a chunk's LDS writes
+  // leaves the next chunk's loads in flight.
+  LocalChunk<PB> c0, c1;
+  if (ch0 < ch1) {
+    load(c0, ch0);
+    int ch = ch0;
+    for (; ch + 2 < ch1; ch += 2) {
+      load(c1, ch + 1);
+      process(c0);
+      load(c0, ch + 2);
+      process(c1);
+    }
+    if (ch + 1 < ch1) {
+      load(c1, ch + 1);
+      process(c0);
+      process(c1);
+    } else {
+      process(c0);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PB; ++p) part[(lw * kLocalSlots + p) * kWave + lane] = acc[p];
+  part[(lw * kLocalSlots + kLocalSlots - 1) * kWave + lane] = accg;
+}
+
 // ---------------------------------------------------------------- GEMM tile
 
 // Static LDS of a GEMM workgroup: the sums of waves 1..3, then flags and the
@@ -393,7 +500,7 @@ __device__ void gather_handoff(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, 
 // ends up under a branch).  ECM: the EC mode (0 none, 1 fused, 2 split), fixed
 // at compile time so the loads of each mode are straight-line code.
 template <int NBW, int CPW, bool EXACT, int ECM>
-__global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
+__global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kThreads) skinny_kernel(SkinnyKArgs a) {
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   __shared__ float4_t red[3][kWave][NBW];
   __shared__ uint32_t flags[2];        // [1] last split
@@ -402,6 +509,17 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
     return;
   }
   constexpr int TN = NBW * 16;
+  // Local EC (waves 4..7): the projection, then the one barrier the weight
+  // waves reach before wave 0 reads the sums (a split-K launch never takes
+  // this mode).
+  unsigned char* local_lds = dyn_lds + gemm_bs_bytes(a.ps, TN) + gemm_pc_bytes(a.rank, a.ps);
+  if (ECM == 3 && threadIdx.x >= kThreads) {
+    const int lw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x - kThreads) / kWave);
+    if (local_pb(a.rank) == 2) ec_local_pass<2>(a, local_lds, lw);
+    else ec_local_pass<4>(a, local_lds, lw);
+    __syncthreads();
+    return;
+  }
   const int b = blockIdx.x - a.P;
   const int s = b / a.T, t = b % a.T;
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -537,6 +655,33 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) acc[nb] += red[i][lane][nb];
   }
+  // Local EC: the four local waves' sums, in fixed order, into Pc (lane
+  // (t4, c16) holds rows 4 t4 .. 4 t4 + 3 of column c16 of each block).
+  if (ECM == 3 && w == 0) {
+    const float4_t* part = reinterpret_cast<const float4_t*>(local_lds + kLocalWaves * local_buf_bytes(a.rank));
+    const int pblocks = (a.rank + 15) / 16;
+    for (int pb = 0; pb < pblocks; ++pb) {
+      float4_t sum = part[pb * kWave + lane];
+#pragma unroll
+      for (int q = 1; q < kLocalWaves; ++q) sum += part[(q * kLocalSlots + pb) * kWave + lane];
+      const int col = pb * 16 + c16;
+      if (col < a.rank) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Pc[(4 * t4 + v) * pcs + col] = sum[v];
+      }
+    }
+    float4_t z = part[(kLocalSlots - 1) * kWave + lane];
+#pragma unroll
+    for (int q = 1; q < kLocalWaves; ++q) z += part[(q * kLocalSlots + kLocalSlots - 1) * kWave + lane];
+    if (c16 == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float g = sigmoidf_(z[v] + a.gate_bias);
+        if (a.skip_tau > 0.0f && !(g >= a.skip_tau)) g = 0.0f;
+        Pc[(4 * t4 + v) * pcs + a.rank] = g;
+      }
+    }
+  }
 
   // ---- S splits -> the last to arrive (wave 0 exchanges, the block follows).
   // Workgroups that are not last count themselves out and leave.
@@ -604,12 +749,12 @@ __global__ void __launch_bounds__(kThreads) skinny_kernel(SkinnyKArgs a) {
   // 8 t4 .. 8 t4 + 7 of each 32-column block (two 16-byte reads of a
   // 16-byte aligned row), times the row's gate, as the A fragment; the B
   // fragment of Bs from two transposing reads.
-  const float* prow = ECM == 1 ? Pc + (size_t)c16 * pcs : reinterpret_cast<const float*>(table) + (size_t)c16 * a.ps;
+  const float* prow = ECM != 2 ? Pc + (size_t)c16 * pcs : reinterpret_cast<const float*>(table) + (size_t)c16 * a.ps;
   float4_t ec[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) ec[nb] = zero_float4();
   if (ECM) {
-    const float gv = c16 < a.M ? (ECM == 1 ? prow[a.rank] : reinterpret_cast<const float*>(table + (size_t)16 * a.ps * 4)[c16])
+    const float gv = c16 < a.M ? (ECM != 2 ? prow[a.rank] : reinterpret_cast<const float*>(table + (size_t)16 * a.ps * 4)[c16])
                                : 0.0f;                   // the final gate g'
     if (__any(gv != 0.0f)) {
       for (int jb = 0; jb < jblocks; ++jb) {
@@ -658,7 +803,12 @@ template <int NBW, int CPW, bool EXACT>
 hipError_t launch_exact(const SkinnyKArgs& k, size_t lds, void* stream) {
   const dim3 grid(k.P + k.T * k.S), block(kThreads);
   hipError_t e = hipSuccess;
-  if (k.ec_mode == 1) {
+  if (k.ec_mode == 3) {
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 3>, NBW>();
+    if (e == hipSuccess)
+      hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 3>), grid, dim3(kThreads + kLocalWaves * kWave), lds,
+                         (hipStream_t)stream, k);
+  } else if (k.ec_mode == 1) {
     e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 1>, NBW>();
     if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 1>), grid, block, lds, (hipStream_t)stream, k);
   } else if (k.ec_mode == 2) {
@@ -723,7 +873,13 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
   sh.CPW = sh.CPW <= 1 ? 1 : sh.CPW <= 2 ? 2 : sh.CPW <= 4 ? 4 : 8;
   const int ps = rank > 0 ? (int)p_stride(rank) : 0;
   const int r1p = (int)round_up(rank + 1, 2);
-  if (fused && rank > 0) {
+  // Local EC (every GEMM workgroup computes the projection itself): no K
+  // split of the weight GEMM, rank % 4 == 0 (transposing LDS reads), rank <=
+  // 64, and an A small enough that every workgroup reading it from L2 costs
+  // less than the producers' hand-off.
+  if (fused && rank > 0 && sh.S == 1 && rank % 4 == 0 && rank <= 64 && (size_t)K * rank * 2 <= kLocalMaxABytes)
+    sh.local_ec = true;
+  if (fused && rank > 0 && !sh.local_ec) {
     // Producer slabs: a power of two near K / 8 (128 .. 1024), halved until
     // one slab's LDS (A slab, w_g slab and column, X slab) fits 64 KiB, so two
     // workgroups fit a CU (every workgroup of the launch gets this LDS).
@@ -737,7 +893,8 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
   }
   if (rank > 0)
     sh.lds_gemm = gemm_bs_bytes(ps, sh.nbw * 16) + gemm_pc_bytes((int)rank, ps) +
-                  gemm_table_bytes(fused ? 1 : 2, ps, r1p, sh.P, (int)M);
+                  gemm_table_bytes(fused ? 1 : 2, ps, r1p, sh.P, (int)M) +
+                  (sh.local_ec ? local_lds_bytes((int)rank) : 0);
   // Workspace: sync words in the counter header and the hand-off slabs in the
   // header's hand-off region; the split-K slots as scratch from scratch_base
   // on.
@@ -768,11 +925,12 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream) {
   k.KC = (int)(k_pad(L.K) / kKChunk);
   k.NBLK = (int)(n_pad(L.N) / kNBlock);
   k.T = sh.T; k.S = sh.S; k.CPS = sh.CPS;
-  k.P = L.ec_mode == 1 ? sh.P : 0;
+  const int ec_mode = L.ec_mode == 1 && sh.local_ec ? 3 : L.ec_mode;
+  k.P = ec_mode == 1 ? sh.P : 0;
   k.ksp = sh.ksp;
   k.ps = L.ec_mode ? (int)p_stride(L.rank) : 0;
   k.r1p = (int)round_up(L.rank + 1, 2);
-  k.ec_mode = L.ec_mode;
+  k.ec_mode = ec_mode;
   k.gate_bias = L.gate_bias; k.skip_tau = L.skip_tau;
   char* ws = (char*)L.workspace;
   k.sync = (uint32_t*)(ws + sh.ws_sync);   // absolute offsets from the workspace base
@@ -781,7 +939,7 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream) {
   k.Pext = L.Pext;
   k.gext = L.gext;
   k.spin_limit = 1u << 20;   // ~0.5 s of polling: far beyond any healthy wait
-  k.stream_delay = L.ec_mode == 1 ? kStreamDelay : 0;
+  k.stream_delay = ec_mode == 1 ? kStreamDelay : 0;
   size_t lds = k.P > 0 ? sh.lds : 0;
   if (L.ec_mode && sh.lds_gemm > lds) lds = sh.lds_gemm;
   const bool exact = sh.CPS == 4 * sh.CPW && (int64_t)sh.CPS * sh.S == k.KC;
