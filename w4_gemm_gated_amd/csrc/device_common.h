@@ -81,7 +81,12 @@ __device__ __forceinline__ half8_t load_half8(const half_t* p) {
 __device__ __forceinline__ uint32_t float_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bits_float(uint32_t x) { return __builtin_bit_cast(float, x); }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+// 1 / (1 + e^-z) from the hardware base-2 exponential and reciprocal (a few
+// ulp; the gate feeds an fp16 product).  z = -inf-like values give 0, large
+// z give 1.
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
 
 // Buffer resource over [base, base + bytes): raw buffer loads at an offset
 // outside it return zeros without touching memory, which masks lanes without

@@ -415,84 +415,116 @@ __host__ __device__ __forceinline__ size_t gemm_table_bytes(int ec_mode, int ps,
 // Thread t takes 16-byte units q = t, t + 256, ... of a slab (two entries of
 // row q / (r1p / 2)) and loads that unit of every slab, Q units x PB slabs
 // in flight at once (one memory round trip per batch).  While any lane of the
-// wave holds a unit whose tag is not yet this call's, the wave reloads the
-// whole batch (bounded wait).  The code has no per-unit branches: offsets of
-// absent units are out of range (they read as zeros) and the tag test is
-// plain arithmetic.  The slabs are added in fixed order and the gate applied
-// to column rank; the result goes to Pc[row][col] (row stride pcs).
+// wave holds a unit whose tag is not yet this call's, the wave requests the
+// whole batch again (bounded wait).  No per-unit branches: offsets of absent
+// units are out of range (they read as zeros) and the tag test is plain
+// arithmetic.  The slabs are added in fixed order and the gate applied to
+// column rank; the result goes to Pc[row][col] (row stride pcs).
+template <int Q, int PB>
+struct HandoffBatch {
+  u32x4_t v[Q][PB];
+  uint32_t off[Q];   // byte offset of the unit in a slab (out of range: no unit)
+  bool two[Q];       // entry 1 of the unit is a real column
+  int row[Q], c0[Q];
+};
+
+template <int Q, int PB>
+__device__ __forceinline__ void handoff_units(const SkinnyKArgs& a, int q0, HandoffBatch<Q, PB>& h) {
+  const int pairs = a.M * a.r1p / 2;                     // 16-byte units per slab
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    const int q = q0 + i * kThreads + (int)threadIdx.x;
+    h.off[i] = q < pairs ? (uint32_t)q * 16u : kOutOfRange;
+    h.row[i] = (2 * q) / a.r1p;
+    h.c0[i] = (2 * q) % a.r1p;
+    h.two[i] = h.c0[i] + 1 < a.rank + 1;
+  }
+}
+
+template <int Q, int PB>
+__device__ __forceinline__ void handoff_load(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, int p0,
+                                             HandoffBatch<Q, PB>& h) {
+  const uint32_t slab_bytes = (uint32_t)a.M * (uint32_t)a.r1p * 8u;
+#pragma unroll
+  for (int i = 0; i < Q; ++i)
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      // off + slab offset stays out of range when off is (no wrap).
+      const uint32_t o = p0 + j < a.P ? h.off[i] + (uint32_t)(p0 + j) * slab_bytes : kOutOfRange;
+      h.v[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, o, 0, kCachePolicySc1));
+    }
+}
+
+template <int Q, int PB>
+__device__ __forceinline__ void handoff_wait(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, uint32_t tag, int p0,
+                                             HandoffBatch<Q, PB>& h) {
+  for (uint32_t n = 0;; ++n) {
+    bool stale = false;
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const bool ready = (h.v[i][j][1] == tag) & (!h.two[i] | (h.v[i][j][3] == tag));
+        stale |= (p0 + j < a.P) & (h.off[i] != kOutOfRange) & !ready;
+      }
+    if (!__any(stale)) break;
+    if (n >= a.spin_limit) {
+      if (threadIdx.x % kWave == 0) st_dev_u32(&a.sync[kError], 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(4);
+    handoff_load(a, hr, p0, h);
+  }
+}
+
+template <int Q, int PB>
+__device__ __forceinline__ void handoff_add(const SkinnyKArgs& a, int p0, const HandoffBatch<Q, PB>& h, float* s0,
+                                            float* s1) {
+#pragma unroll
+  for (int i = 0; i < Q; ++i)
+#pragma unroll
+    for (int j = 0; j < PB; ++j)
+      if (p0 + j < a.P) {
+        s0[i] += bits_float(h.v[i][j][0]);
+        s1[i] += bits_float(h.v[i][j][2]);
+      }
+}
+
+template <int Q, int PB>
+__device__ __forceinline__ void handoff_store(const SkinnyKArgs& a, const HandoffBatch<Q, PB>& h, const float* s0,
+                                              const float* s1, float* Pc, int pcs) {
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    if (h.off[i] == kOutOfRange) continue;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int col = h.c0[i] + e;
+      if (col > a.rank) continue;
+      float v = e == 0 ? s0[i] : s1[i];
+      if (col == a.rank) {
+        v = sigmoidf_(v + a.gate_bias);
+        if (a.skip_tau > 0.0f && !(v >= a.skip_tau)) v = 0.0f;
+      }
+      Pc[h.row[i] * pcs + col] = v;
+    }
+  }
+}
+
 template <int Q, int PB>
 __device__ void gather_handoff(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, uint32_t tag, float* Pc, int pcs) {
-  const int tid = threadIdx.x;
-  const int r1 = a.rank + 1;
-  const int pairs = a.M * a.r1p / 2;                     // 16-byte units per slab
-  const uint32_t slab_bytes = (uint32_t)a.M * (uint32_t)a.r1p * 8u;
+  const int pairs = a.M * a.r1p / 2;
   for (int q0 = 0; q0 < pairs; q0 += Q * kThreads) {
+    HandoffBatch<Q, PB> h;
+    handoff_units(a, q0, h);
     float s0[Q], s1[Q];
-    uint32_t off[Q];
-    bool two[Q];                                         // entry 1 is a real column
 #pragma unroll
-    for (int i = 0; i < Q; ++i) {
-      const int q = q0 + i * kThreads + tid;
-      s0[i] = s1[i] = 0.0f;
-      off[i] = q < pairs ? (uint32_t)q * 16u : kOutOfRange;
-      two[i] = (2 * q) % a.r1p + 1 < r1;
-    }
+    for (int i = 0; i < Q; ++i) s0[i] = s1[i] = 0.0f;
     for (int p0 = 0; p0 < a.P; p0 += PB) {
-      u32x4_t v[Q][PB];
-      auto issue = [&]() {
-#pragma unroll
-        for (int i = 0; i < Q; ++i)
-#pragma unroll
-          for (int j = 0; j < PB; ++j) {
-            // off + slab offset stays out of range when off is (no wrap).
-            const uint32_t o = p0 + j < a.P ? off[i] + (uint32_t)(p0 + j) * slab_bytes : kOutOfRange;
-            v[i][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(hr, o, 0, kCachePolicySc1));
-          }
-      };
-      issue();
-      for (uint32_t n = 0;; ++n) {
-        bool stale = false;
-#pragma unroll
-        for (int i = 0; i < Q; ++i)
-#pragma unroll
-          for (int j = 0; j < PB; ++j) {
-            const bool ready = (v[i][j][1] == tag) & (!two[i] | (v[i][j][3] == tag));
-            stale |= (p0 + j < a.P) & (off[i] != kOutOfRange) & !ready;
-          }
-        if (!__any(stale)) break;
-        if (n >= a.spin_limit) {
-          if (tid % kWave == 0) st_dev_u32(&a.sync[kError], 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(4);
-        issue();
-      }
-#pragma unroll
-      for (int i = 0; i < Q; ++i)
-#pragma unroll
-        for (int j = 0; j < PB; ++j)
-          if (p0 + j < a.P) {
-            s0[i] += bits_float(v[i][j][0]);
-            s1[i] += bits_float(v[i][j][2]);
-          }
+      handoff_load(a, hr, p0, h);
+      handoff_wait(a, hr, tag, p0, h);
+      handoff_add(a, p0, h, s0, s1);
     }
-#pragma unroll
-    for (int i = 0; i < Q; ++i) {
-      const int q = q0 + i * kThreads + tid;
-      if (q >= pairs) continue;
-      const int row = (2 * q) / a.r1p, c0 = (2 * q) % a.r1p;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int col = c0 + e;
-        if (col >= r1) continue;
-        float v = e == 0 ? s0[i] : s1[i];
-        if (col == a.rank) {
-          v = sigmoidf_(v + a.gate_bias);
-          if (a.skip_tau > 0.0f && !(v >= a.skip_tau)) v = 0.0f;
-        }
-        Pc[row * pcs + col] = v;
-      }
-    }
+    handoff_store(a, h, s0, s1, Pc, pcs);
   }
 }
 
@@ -723,12 +755,11 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
   // ---- fused: gather the producers' slabs, check their tags (units not yet
   // published are reloaded, bounded wait), add them and apply the gate.
   if (ECM == 1) {
-    const __amdgpu_buffer_rsrc_t hr =
-        make_rsrc(a.handoff, (uint32_t)((size_t)a.P * a.M * a.r1p * 8));
     // The whole table after the matrix instructions.  (Requested any
     // earlier, the loads would queue behind the weight stream and be served
     // about when it is, normally just before the producers publish, which
     // costs a second round trip.)  Sixteen loads in flight per thread.
+    const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.handoff, (uint32_t)((size_t)a.P * a.M * a.r1p * 8));
     if (a.P <= 8) gather_handoff<2, 8>(a, hr, tag, Pc, pcs);
     else gather_handoff<1, 16>(a, hr, tag, Pc, pcs);
     __syncthreads();
