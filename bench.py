@@ -15,7 +15,13 @@ on (torch's current stream).
 Also reported on the same line: per-token-count times and the EC overhead
 (same calls with the EC switched off), the prefill workload (M = 2048,
 K = 4096, N = 14336, rank 64) in TFLOP/s against the fp16 matrix-core peak,
-and the fp64 oracle timed on the host cores on a bounded sample.
+and the fp64 oracle timed on the host cores on a bounded sample.  Under
+"mid_m", the mid-size token counts: the mixed-gate down_proj (M = 64 and
+512, K = 14336, N = 4096, rank 64; FUSED, SPLIT and EC off, skip threshold
+0 and 0.05; the FUSED/SPLIT crossover and the fraction of the binding
+roofline) and the small-model layer stack (256 tokens, seven linears, the EC
+on four of them; per-layer latency with the EC on and off).  These are
+reported beside the headline, never as `value`.
 """
 import argparse
 import json
@@ -37,6 +43,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mid", action="store_true", help="skip the mid-size-M configurations")
+    ap.add_argument("--mid-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--pmc-mode", action="store_true",
@@ -64,7 +72,7 @@ class Layer:
             if i == 0:
                 self.sets.append((Wq, s, A, B, wg))
             else:
-                self.sets.append(tuple(x.clone() for x in (Wq, s, A, B, wg)))
+                self.sets.append(tuple(None if x is None else x.clone() for x in (Wq, s, A, B, wg)))
         self.X = t(w["X"])
         self.K, self.N, self.r = w["K"], w["N"], w["r"]
 
@@ -302,6 +310,11 @@ def main():
         log(f"prefill: {t_on * 1e6:.1f} us, {tf:.1f} TFLOP/s; EC off {t_off * 1e6:.1f} us")
         del pre, pYs
 
+    # ------------------------------------------------------------ mid-size M
+    mid = None
+    if not args.no_mid:
+        mid = mid_size(torch, sp, workloads, args.mid_steps, graph)
+
     # ------------------------------------------------------------ oracle on the host
     cpu = None
     if not args.no_cpu_baseline:
@@ -330,8 +343,91 @@ def main():
         "per_m": per_m,
         "ec_overhead": overhead,
         "prefill": prefill,
+        "mid_m": mid,
     }
     print(json.dumps(line), flush=True)
+
+
+def mid_size(torch, sp, workloads, steps, graph):
+    """Mid-size M: the mixed-gate down_proj (config of M = 64 and 512) and the
+    layer stack (M = 256), cold weights (R copies, R x bytes >= 512 MiB)."""
+    dev = "cuda:0"
+
+    def timed(layer, M, variant, b_g, tau, plan, Ys, ws):
+        X = layer.X[:M]
+
+        def call(i):
+            Wq, s, A, B, wg = layer.sets[i % len(layer.sets)]
+            if variant == "no_ec" or A is None:
+                A = B = wg = None
+            sp.spear_w4ec_linear(X, Wq, s, A, B, wg, b_g, tau, variant, N=layer.N, plan=plan,
+                                 Y=Ys[i % len(Ys)][:M], workspace=ws)
+        return time_calls(torch, [call], steps, 3, graph)
+
+    out = {}
+    w = workloads.workload(4)
+    per_set = workloads.algorithmic_bytes(64, w["K"], w["N"], w["r"])
+    copies = max(2, -(-COLD_BYTES // per_set))
+    log(f"mid-size M: mixed-gate down_proj, {copies} weight copies")
+    lay = Layer(torch, sp, w, copies)
+    Ys = [torch.empty((max(w["ms"]), w["N"]), dtype=torch.float16, device=dev) for _ in range(2)]
+    rows = {}
+    for M in w["ms"]:
+        b_g = w["b_g"][M]
+        plans = {v: sp.spear_dispatch_plan(M, w["K"], w["N"], w["r"] if v != "no_ec" else 0, b_g, 0.0, v)
+                 for v in ("fused", "split", "no_ec")}
+        ws = torch.zeros(max(max(p.workspace_bytes for p in plans.values()), 1 << 20), dtype=torch.uint8,
+                         device=dev)
+        r = {}
+        for tau in w["taus"]:
+            for v in ("fused", "split"):
+                r[f"{v}_us" + ("" if tau == 0.0 else f"_tau{tau:g}")] = round(
+                    timed(lay, M, v, b_g, tau, plans[v], Ys, ws) * 1e6, 2)
+        r["no_ec_us"] = round(timed(lay, M, "no_ec", 0.0, 0.0, plans["no_ec"], Ys, ws) * 1e6, 2)
+        best = min(r["fused_us"], r["split_us"])
+        r["faster"] = "fused" if r["fused_us"] <= r["split_us"] else "split"
+        r["ec_overhead"] = round(best / r["no_ec_us"] - 1.0, 4)
+        nbytes = workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"])
+        main_f, _ = workloads.algorithmic_flops(M, w["K"], w["N"], w["r"])
+        if M == 64:
+            r["bound"] = "hbm"
+            r["frac"] = round(nbytes / (best * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        else:
+            r["bound"] = "mfma"
+            r["frac"] = round(main_f / (best * 1e-6) / 1e12 / MFMA_FP16_PEAK_TFS, 4)
+        rows[str(M)] = r
+        log(f"mid-size M={M}: fused {r['fused_us']} us, split {r['split_us']} us, EC off {r['no_ec_us']} us")
+    out["mixed_gate_down_proj"] = {"K": w["K"], "N": w["N"], "rank": w["r"], "weight_copies": copies,
+                                   "per_m": rows}
+    del lay
+
+    layers = [workloads.stack_layer(i) for i in range(7)]
+    per_set = sum(workloads.algorithmic_bytes(256, L["K"], L["N"], L["r"] if L["A"] is not None else 0)
+                  for L in layers)
+    copies = max(2, -(-COLD_BYTES // per_set))
+    log(f"mid-size M: layer stack (256 tokens), {copies} weight copies")
+    st = {}
+    total_on = total_off = 0.0
+    for L in layers:
+        lay = Layer(torch, sp, L, copies)
+        M, ec = 256, L["A"] is not None
+        Ys = [torch.empty((M, L["N"]), dtype=torch.float16, device=dev) for _ in range(2)]
+        p_on = sp.spear_dispatch_plan(M, L["K"], L["N"], L["r"] if ec else 0, 0.0, 0.0, "auto")
+        p_off = sp.spear_dispatch_plan(M, L["K"], L["N"], 0, 0.0, 0.0, "no_ec")
+        ws = torch.zeros(max(p_on.workspace_bytes, p_off.workspace_bytes, 1 << 20), dtype=torch.uint8, device=dev)
+        t_off = timed(lay, M, "no_ec", 0.0, 0.0, p_off, Ys, ws)
+        t_on = timed(lay, M, "auto", 0.0, 0.0, p_on, Ys, ws) if ec else t_off
+        total_on += t_on
+        total_off += t_off
+        st[L["name"]] = {"K": L["K"], "N": L["N"], "ec": ec, "us": round(t_on * 1e6, 2),
+                         "no_ec_us": round(t_off * 1e6, 2),
+                         "variant": _binding_variant(p_on) if ec else "no_ec",
+                         "ec_overhead": round(t_on / t_off - 1.0, 4) if ec else 0.0}
+        del lay
+    out["layer_stack"] = {"tokens": 256, "weight_copies": copies, "layers": st,
+                          "stack_us": round(total_on * 1e6, 2), "stack_no_ec_us": round(total_off * 1e6, 2)}
+    log(f"mid-size M: layer stack {total_on * 1e6:.1f} us, EC off {total_off * 1e6:.1f} us")
+    return out
 
 
 def _binding_variant(plan):
