@@ -609,8 +609,18 @@ TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_
   return t;
 }
 
+TiledShape fused_tiled_shape(int64_t M, int64_t K, int64_t N, int cus, int ec_blocks, size_t scratch_base) {
+  const int left = cus - ec_blocks > cus / 2 ? cus - ec_blocks : cus / 2;
+  const TiledShape t = tiled_shape(M, K, N, left, scratch_base);
+  if ((int64_t)t.grid * 3 >= (int64_t)cus * 2) return t;
+  return tiled_shape(M, K, N, cus, scratch_base);
+}
+
 hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream) {
-  const TiledShape t = tiled_shape(a.M, a.K, a.N, plan.cus, a.scratch_base);
+  const EcWorkspace ecl = a.fused ? ec_workspace_layout(a.M, a.K, a.rank, kEcBlocksFused) : EcWorkspace{};
+  const int ec_blocks = a.fused ? (int)round_up(ecl.m_tiles * ecl.splits, 8) : 0;
+  const TiledShape t = a.fused ? fused_tiled_shape(a.M, a.K, a.N, plan.cus, ec_blocks, a.scratch_base)
+                               : tiled_shape(a.M, a.K, a.N, plan.cus, a.scratch_base);
   GemmKArgs k;
   k.X = (const half_t*)a.X;
   k.Wq = (const u32x4_t*)a.Wq;
@@ -636,7 +646,7 @@ hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream
   if (a.fused) {
     // EC workgroups first (P and g into the EC workspace, ready flags in the
     // EC counter region), then the GEMM tiles.
-    const EcWorkspace L = ec_workspace_layout(a.M, a.K, a.rank, kEcBlocksFused);
+    const EcWorkspace& L = ecl;
     FusedKArgs f;
     f.e = make_ec_kargs(a.ecargs, L);
     f.e.ready = (uint32_t*)a.workspace + kEcReadyWord;

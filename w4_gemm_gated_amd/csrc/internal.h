@@ -158,6 +158,11 @@ struct TiledShape {
 };
 // scratch_base: first byte of the workspace this kernel may use as scratch.
 TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_base);
+// The tiles of a fused tiled launch, whose ec_blocks EC workgroups lead the
+// grid and hold their CUs: the K split is planned for the CUs they leave free
+// (else a second wave of tiles waits for a free CU), unless the tiles would
+// then cover less than two thirds of the GPU.
+TiledShape fused_tiled_shape(int64_t M, int64_t K, int64_t N, int cus, int ec_blocks, size_t scratch_base);
 
 hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);

@@ -94,7 +94,8 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     // X and the packed weight are addressed with 32-bit buffer offsets.
     if ((int64_t)d.M * d.K * 2 > INT32_MAX || n_pad(d.N) * k_pad(d.K) / 2 > INT32_MAX)
       return SPEAR_ERR_UNSUPPORTED;
-    const TiledShape t = tiled_shape(d.M, d.K, d.N, cus, scratch_base);
+    const TiledShape t = p.variant == SPEAR_VARIANT_FUSED ? fused_tiled_shape(d.M, d.K, d.N, cus, ec_blocks, scratch_base)
+                                                          : tiled_shape(d.M, d.K, d.N, cus, scratch_base);
     if (!t.fits) return SPEAR_ERR_UNSUPPORTED;
     p.kernel = 1;
     p.tile_m = t.tm; p.tile_n = t.tn;
