@@ -6,7 +6,10 @@
 //   * no EC (rank 0) or variant NO_EC            -> NO_EC: the W4 GEMM alone;
 //   * AUTO and rank % 4 == 0                     -> FUSED: one launch (EC
 //     workgroups first, then the W4 GEMM with the gated epilogue, which
-//     waits for the EC results it needs);
+//     waits for the EC results it needs; at M <= 16 the EC computed by every
+//     GEMM workgroup itself when A is small), except 128-row tiles whose
+//     fused launch would exceed the CUs (M of about 257 to 1024), where the
+//     measured crossover favours SPLIT;
 //   * AUTO otherwise (rank % 4 != 0)             -> SPLIT (EC projection
 //     launch, then the W4 GEMM with the gated epilogue);
 //   * the per-token gate-value decision (skip the EC term where every gate of
@@ -51,10 +54,23 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank, kEcBlocksFused);
     return L.m_tiles <= kMaxEcTiles;
   };
+  // Measured crossover (mid M, cold weights): with 128-row tiles whose fused
+  // launch needs more workgroups than CUs (M of about 512 to 1024), the split
+  // variant is as fast or faster (M = 512, K = 4096, N = 14336: 87.9 vs
+  // 94.0 us; M = 1024, K = 14336, N = 4096: 173 vs 184 us); with 64-row tiles
+  // (M <= 256) and 256-row tiles the fused one is (M = 256: 54.6 vs 62.8 us;
+  // M = 2048: 257 vs 267 us).
+  auto split_wins = [&]() {
+    if (skinny) return false;
+    const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank, kEcBlocksFused);
+    const int eb = (int)round_up(L.m_tiles * L.splits, 8);
+    const TiledShape t = fused_tiled_shape(d.M, d.K, d.N, cus, eb, kSyncHeaderBytes);
+    return t.tm == 128 && t.grid + eb > cus;
+  };
   if (!ec) {
     p.variant = SPEAR_VARIANT_NO_EC;
   } else if (d.variant == SPEAR_VARIANT_AUTO) {
-    p.variant = fused_ok() ? SPEAR_VARIANT_FUSED : SPEAR_VARIANT_SPLIT;
+    p.variant = fused_ok() && !split_wins() ? SPEAR_VARIANT_FUSED : SPEAR_VARIANT_SPLIT;
   } else {
     p.variant = d.variant;
   }
