@@ -202,6 +202,8 @@ def test_local_ec_ragged_shapes(M, K, N, r):
     p = sp.spear_dispatch_plan(M, K, N, r, 0.4, variant="fused")
     assert p.ec_local == 1 and p.producers == 0
     layer_case(X, W, A, B, w_g, 0.4, 0.0, "fused", f"local EC M={M} K={K} N={N} r={r}")
+    # the device-side skip: tokens whose gate is below tau get no EC term
+    layer_case(X, W, A, B, w_g, 0.4, 0.6, "fused", f"local EC M={M} K={K} N={N} r={r} tau=0.6")
 
 
 @pytest.mark.parametrize("variant", ["fused", "split"])
