@@ -67,11 +67,11 @@ def plan(lib, M, K, N, r, variant=0, cus=256, bias=0.0, tau=0.0):
 def test_dispatch_rules(lib):
     st, p = plan(lib, 16, 4096, 4096, 32)
     assert st == 0 and p.variant == 1 and p.kernel == 0
-    # tiled fused: about 64 EC workgroups (32 row tiles x 2 K slices) lead
+    # tiled fused: about 128 EC workgroups (32 row tiles x 4 K slices) lead
     # the grid, then the 8 x 64 tiles of 256 x 224
     st, p = plan(lib, 2048, 4096, 14336, 64)
     assert st == 0 and p.variant == 1 and p.kernel == 1 and p.workspace_bytes > 0
-    assert p.producers == 32 * 2 and p.grid == 64 + 8 * 64 and p.tile_m == 256 and p.tile_n == 224
+    assert p.producers == 32 * 4 and p.grid == 128 + 8 * 64 and p.tile_m == 256 and p.tile_n == 224
     st, p = plan(lib, 2048, 4096, 14336, 64, variant=2)
     assert st == 0 and p.variant == 2 and p.kernel == 1 and p.grid == 8 * 64
     # EC workgroups are padded to a multiple of 8 (the GEMM tiles keep their
