@@ -129,9 +129,8 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
  * Rules: rank 0 or variant NO_EC -> NO_EC; AUTO -> FUSED when rank % 4 == 0
  * (any M: the skinny kernel up to 16 rows, the tiled kernel above, both with
  * the EC projection in the same launch), except where the tiled kernel uses
- * 128-row tiles (M of about 257 to 1024) and the fused launch would need more
- * workgroups than the GPU has CUs (measured: SPLIT as fast or faster there);
- * else SPLIT.  Skinny FUSED takes
+ * 128-row tiles (M of about 257 to 1024) that alone exceed the GPU's CUs
+ * (measured: SPLIT faster there); else SPLIT.  Skinny FUSED takes
  * one of two forms, reported by plan.ec_local: when the weight GEMM needs no
  * K split, rank <= 64 and A is at most 128 KiB, every GEMM workgroup
  * computes the whole projection itself with four extra waves (ec_local = 1,

@@ -78,11 +78,12 @@ def test_dispatch_rules(lib):
     # XCD order): 1 row tile x 14 K slices -> 16
     st, p = plan(lib, 64, 14336, 4096, 64)
     assert st == 0 and p.variant == 1 and p.producers == 14 and p.grid == 16 + 32 * p.split_k
-    # 128-row tiles whose fused launch would exceed the CUs: auto takes split
+    # 128-row tiles that alone exceed the CUs: auto takes split; where the
+    # tiles fit, fused (even when its EC workgroups overflow the CUs)
+    st, p = plan(lib, 512, 4096, 14336, 64)
+    assert st == 0 and p.variant == 2 and p.tile_m == 128 and p.grid > 256
     st, p = plan(lib, 512, 14336, 4096, 64)
-    assert st == 0 and p.variant == 2 and p.tile_m == 128
-    st, p = plan(lib, 512, 14336, 4096, 64, variant=1)
-    assert st == 0 and p.variant == 1 and p.grid > 256
+    assert st == 0 and p.variant == 1 and p.tile_m == 128 and p.grid > 256
     st, p = plan(lib, 256, 2048, 8192, 32)
     assert st == 0 and p.variant == 1 and p.tile_m == 64
     st, p = plan(lib, 16, 4096, 4096, 32)

@@ -54,18 +54,19 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank, kEcBlocksFused);
     return L.m_tiles <= kMaxEcTiles;
   };
-  // Measured crossover (mid M, cold weights): with 128-row tiles whose fused
-  // launch needs more workgroups than CUs (M of about 512 to 1024), the split
-  // variant is as fast or faster (M = 512, K = 4096, N = 14336: 87.9 vs
-  // 94.0 us; M = 1024, K = 14336, N = 4096: 173 vs 184 us); with 64-row tiles
-  // (M <= 256) and 256-row tiles the fused one is (M = 256: 54.6 vs 62.8 us;
-  // M = 2048: 257 vs 267 us).
+  // Measured crossover (mid M, hot weights, 128 EC workgroups): with
+  // 128-row tiles that alone exceed the CUs the split variant is faster
+  // (M = 512, K = 4096, N = 14336: 87 vs 94 us); where the tiles fit, the
+  // fused one is, also when its EC workgroups overflow the CUs (M = 512,
+  // K = 14336, N = 4096: 98 vs 104 us; M = 768: 153 vs 161; M = 1024: 163 vs
+  // 172; M = 1024, K = N = 4096: 57 vs 61; M = 512, K = 2048, N = 8192: a
+  // tie), as with 64-row (M <= 256) and 256-row tiles.
   auto split_wins = [&]() {
     if (skinny) return false;
     const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank, kEcBlocksFused);
     const int eb = (int)round_up(L.m_tiles * L.splits, 8);
     const TiledShape t = fused_tiled_shape(d.M, d.K, d.N, cus, eb, kSyncHeaderBytes);
-    return t.tm == 128 && t.grid + eb > cus;
+    return t.tm == 128 && t.grid > cus;
   };
   if (!ec) {
     p.variant = SPEAR_VARIANT_NO_EC;
