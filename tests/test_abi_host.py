@@ -88,8 +88,11 @@ def test_dispatch_rules(lib):
     assert st == 0 and p.variant == 1 and p.tile_m == 64
     st, p = plan(lib, 16, 4096, 4096, 32)
     # fused, A of 256 KiB: the EC producer workgroups, then the GEMM tiles
-    # (256 panels of 16 columns, one K range); P goes over through the workspace
-    assert p.variant == 1 and p.ec_local == 0 and p.producers == 8 and p.grid == 256 + 8 and p.split_k == 1
+    # (128 tiles of two 16-column panels, two K ranges); P goes over through
+    # the workspace
+    assert p.variant == 1 and p.ec_local == 0 and p.producers == 8 and p.grid == 256 + 8
+    # two 16-column panels and two K splits per workgroup (same count)
+    assert p.split_k == 2 and p.tile_n == 32
     assert p.workspace_bytes > 0
     # fused, local EC: one K range and an A of at most 128 KiB, so every GEMM
     # workgroup computes the projection itself; no producers, no workspace

@@ -718,12 +718,14 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
   // ---- S splits -> the last to arrive (wave 0 exchanges, the block follows).
   // Workgroups that are not last count themselves out and leave.
   if (a.S > 1) {
+    // One 16-byte device-coherent store / load per lane and panel.
+    const __amdgpu_buffer_rsrc_t gpr = make_rsrc(a.gemm_part, (uint32_t)((size_t)a.T * a.S * NBW * kWave * 16));
     if (w == 0) {
-      float* slot = a.gemm_part + ((size_t)(t * a.S + s) * NBW) * kWave * 4;
+      const uint32_t slot = (uint32_t)((t * a.S + s) * NBW) * kWave * 16u;
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) st_dev(&slot[(nb * kWave + lane) * 4 + v], acc[nb][v]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[nb]), gpr,
+                                               slot + (uint32_t)(nb * kWave + lane) * 16u, 0, kCachePolicySc1);
       drain_vm();
       if (lane == 0) flags[1] = (add_dev_u32(&a.sync[kTiles + t], 1u) == (uint32_t)(a.S - 1)) ? 1u : 0u;
     }
@@ -742,11 +744,9 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) acc[nb] = zero_float4();
       for (int ss = 0; ss < a.S; ++ss) {
-        const float* sl = a.gemm_part + ((size_t)(t * a.S + ss) * NBW) * kWave * 4;
+        const uint32_t sl = (uint32_t)((t * a.S + ss) * NBW) * kWave * 16u;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[nb][v] += ld_dev(&sl[(nb * kWave + lane) * 4 + v]);
+        for (int nb = 0; nb < NBW; ++nb) acc[nb] += buffer_load_f4_dev(gpr, sl + (uint32_t)(nb * kWave + lane) * 16u);
       }
       if (lane == 0) st_dev_u32(&a.sync[kTiles + t], 0u);
     }
@@ -900,16 +900,32 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
       }
     }
   }
-  // Round CPW up to an instantiated value.
-  sh.CPW = sh.CPW <= 1 ? 1 : sh.CPW <= 2 ? 2 : sh.CPW <= 4 ? 4 : 8;
-  const int ps = rank > 0 ? (int)p_stride(rank) : 0;
-  const int r1p = (int)round_up(rank + 1, 2);
   // Local EC (every GEMM workgroup computes the projection itself): no K
   // split of the weight GEMM, rank % 4 == 0 (transposing LDS reads), rank <=
   // 64, and an A small enough that every workgroup reading it from L2 costs
   // less than the producers' hand-off.
-  if (fused && rank > 0 && sh.S == 1 && rank % 4 == 0 && rank <= 64 && (size_t)K * rank * 2 <= kLocalMaxABytes)
-    sh.local_ec = true;
+  auto local_ok = [&]() {
+    return fused && rank > 0 && sh.S == 1 && rank % 4 == 0 && rank <= 64 && (size_t)K * rank * 2 <= kLocalMaxABytes;
+  };
+  // Fused with the hand-off, where the search gives one 16-column panel and
+  // no K split per workgroup: two panels and two K splits keep the workgroup
+  // count and halve the X each workgroup reads and the hand-off gathers (only
+  // the last split of a tile runs the epilogue).  Measured on 4096 x 4096,
+  // rank 32: M = 16 11.35 -> 10.27 us, M = 1 9.48 -> 9.34 us.  Where the
+  // search already splits K, doubling the split was slower (2048 x 2048,
+  // 8192 x 2048, 14336 x 4096).
+  if (fused && rank > 0 && !local_ok() && sh.nbw == 1 && sh.S == 1 && KC % 2 == 0 && KC / 2 <= 4 * kMaxCpw) {
+    sh.nbw = 2;
+    sh.S = 2;
+    sh.T = (int)ceil_div(NBLK, 2);
+    sh.CPS = (int)(KC / 2);
+    sh.CPW = (int)ceil_div(sh.CPS, 4);
+  }
+  // Round CPW up to an instantiated value.
+  sh.CPW = sh.CPW <= 1 ? 1 : sh.CPW <= 2 ? 2 : sh.CPW <= 4 ? 4 : 8;
+  const int ps = rank > 0 ? (int)p_stride(rank) : 0;
+  const int r1p = (int)round_up(rank + 1, 2);
+  if (local_ok()) sh.local_ec = true;
   if (fused && rank > 0 && !sh.local_ec) {
     // Producer slabs: a power of two near K / 8 (128 .. 1024), halved until
     // one slab's LDS (A slab, w_g slab and column, X slab) fits 64 KiB, so two
