@@ -37,7 +37,11 @@ namespace spear {
 namespace {
 
 constexpr int kThreads = 256;          // four waves
-constexpr uint32_t kStreamDelay = 16;  // fused: GEMM head-start delay, in s_sleep 1 units (64 clocks)
+// Fused: the GEMM workgroups' delay before their weight stream (the
+// producers' head start), in s_sleep 1 units (64 clocks).  Measured on
+// 4096 x 4096, rank 32, two panels and two K splits per workgroup (M = 1 /
+// 16, us): 0: 8.5 / 10.4; 8: 8.7 / 9.8; 16: 8.9 / 9.9; 32: 9.4 / 10.3.
+constexpr uint32_t kStreamDelay = 8;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Sync words of the GEMM half of the counter header, each hot one on its own
