@@ -132,7 +132,8 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
  * 128-row tiles (M of about 257 to 1024) that alone exceed the GPU's CUs
  * (measured: SPLIT faster there); else SPLIT.  Skinny FUSED takes
  * one of two forms, reported by plan.ec_local: when the weight GEMM needs no
- * K split, rank <= 64 and A is at most 128 KiB, every GEMM workgroup
+ * K split, rank <= 64 and A is at most 64 KiB (128 KiB with rank <= 32 and
+ * M <= 4), every GEMM workgroup
  * computes the whole projection itself with four extra waves (ec_local = 1,
  * producers = 0, no workspace); otherwise producer workgroups lead the grid
  * and hand P and the gate over through the workspace (ec_local = 0).  FUSED with

@@ -94,12 +94,20 @@ def test_dispatch_rules(lib):
     # two 16-column panels and two K splits per workgroup (same count)
     assert p.split_k == 2 and p.tile_n == 32
     assert p.workspace_bytes > 0
-    # fused, local EC: one K range and an A of at most 128 KiB, so every GEMM
-    # workgroup computes the projection itself; no producers, no workspace
-    st, p = plan(lib, 16, 2048, 4096, 32)
+    # fused, local EC: one K range and an A of at most 64 KiB (128 KiB with
+    # rank <= 32 and M <= 4), so every GEMM workgroup computes the projection
+    # itself; no producers, no workspace
+    st, p = plan(lib, 4, 2048, 4096, 32)
     assert st == 0 and p.ec_local == 1 and p.producers == 0 and p.grid == 256 and p.workspace_bytes == 0
-    st, p = plan(lib, 1, 1024, 14336, 64)
+    st, p = plan(lib, 16, 1024, 4096, 32)
+    assert st == 0 and p.ec_local == 1 and p.producers == 0
+    st, p = plan(lib, 1, 512, 14336, 64)
     assert st == 0 and p.ec_local == 1 and p.split_k == 1
+    # 128 KiB with 16 rows, or with rank 64: the hand-off
+    st, p = plan(lib, 16, 2048, 4096, 32)
+    assert st == 0 and p.ec_local == 0 and p.producers > 0
+    st, p = plan(lib, 1, 1024, 14336, 64)
+    assert st == 0 and p.ec_local == 0 and p.producers > 0
     st, p = plan(lib, 16, 4096, 14336, 64)
     assert st == 0 and p.ec_local == 0 and p.producers > 0       # A of 512 KiB: hand-off
     # fused with a K split: producer workgroups lead the grid

@@ -192,12 +192,13 @@ def test_fused_ragged_shapes(M, K, N, r):
 
 
 @pytest.mark.parametrize("M,K,N,r", [(3, 1000, 4096, 20), (7, 264, 4096, 36), (2, 520, 4096, 4),
-                                     (5, 1032, 6000, 52), (16, 1024, 14336, 64), (16, 2048, 4096, 32)])
+                                     (5, 616, 6000, 52), (16, 512, 14336, 64), (4, 2048, 4096, 32)])
 def test_local_ec_ragged_shapes(M, K, N, r):
     """The fused skinny launch with the local EC (every workgroup computes the
     projection itself): K tails inside the last chunk of A, partial column
     blocks of A, the two chunk shapes (rank <= 32 and <= 64), a partial last
-    column panel and the largest A the planner keeps local (128 KiB)."""
+    column panel and the largest A the planner keeps local (64 KiB at rank 64,
+    128 KiB at rank 32 with 4 rows)."""
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=13 * M + K + N + r, outliers=True)
     p = sp.spear_dispatch_plan(M, K, N, r, 0.4, variant="fused")
     assert p.ec_local == 1 and p.producers == 0
@@ -265,7 +266,7 @@ def test_local_ec_repeat_calls():
     """A decode shape with a small A: every GEMM workgroup computes the EC
     projection itself (no producers, no workspace); two calls give identical
     results."""
-    M, K, N, r = 16, 2048, 4096, 32
+    M, K, N, r = 16, 1024, 4096, 32
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=19, outliers=True)
     Wq_d, s_d = sp.spear_pack_w4(cuda(W))
     p = sp.spear_dispatch_plan(M, K, N, r, -1.0)

@@ -292,10 +292,16 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
 
 constexpr int kLocalWaves = 4;
 constexpr int kLocalSlots = 5;       // P column blocks (up to four), then the gate
-// A read by every workgroup (from L2).  Measured crossover against the
-// hand-off on a 4096-column decode: local wins by 2.3-2.5 us at 64 KiB of A,
-// slightly at 128 KiB, and loses by 2.6-3.2 us at 256 KiB.
+// A read by every workgroup (from L2).  Measured against the hand-off (two
+// panels and two K splits, 16-byte partials; us, M = 1 / 16, local vs
+// hand-off): 64 KiB of A, local always (1024 x 4096 r 32: 5.0 / 6.2, about
+// 2.5 ahead); 128 KiB, local only for rank <= 32 and few rows (2048 x 4096
+// r 32: 7.0 / 8.9 vs 7.5 / 8.2; 2048 x 8192: 8.4 / 9.9 vs 9.0 / 9.9;
+// 1024 x 14336 r 64: 12.6 / 14.2 vs 11.2 / 13.1); 256 KiB, hand-off (by
+// 2.6-3.2).
 constexpr size_t kLocalMaxABytes = 128 * 1024;
+constexpr size_t kLocalAnyABytes = 64 * 1024;
+constexpr int64_t kLocalMaxRows = 4;            // rows up to which 128 KiB stays local
 constexpr size_t kLocalBufBytes = 8 * 1024;      // one chunk: 8 units of 16 bytes per lane
 __host__ __device__ __forceinline__ int local_pb(int rank) { return rank <= 32 ? 2 : 4; }
 __host__ __device__ __forceinline__ size_t local_buf_bytes(int) { return kLocalBufBytes; }
@@ -909,7 +915,9 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
   // 64, and an A small enough that every workgroup reading it from L2 costs
   // less than the producers' hand-off.
   auto local_ok = [&]() {
-    return fused && rank > 0 && sh.S == 1 && rank % 4 == 0 && rank <= 64 && (size_t)K * rank * 2 <= kLocalMaxABytes;
+    const size_t a_bytes = (size_t)K * rank * 2;
+    return fused && rank > 0 && sh.S == 1 && rank % 4 == 0 && rank <= 64 &&
+           (a_bytes <= kLocalAnyABytes || (a_bytes <= kLocalMaxABytes && rank <= 32 && M <= kLocalMaxRows));
   };
   // Fused with the hand-off, where the search gives one 16-column panel and
   // no K split per workgroup: two panels and two K splits keep the workgroup
