@@ -41,7 +41,8 @@ constexpr int kThreads = 256;          // four waves
 // producers' head start), in s_sleep 1 units (64 clocks).  Measured on
 // 4096 x 4096, rank 32, two panels and two K splits per workgroup (M = 1 /
 // 16, us): 0: 8.5 / 10.4; 8: 8.7 / 9.8; 16: 8.9 / 9.9; 32: 9.4 / 10.3.
-// A single row takes none (its producers' slabs are the smallest).
+// Up to four rows take none (M = 2: 8.7 vs 8.9 us; M = 4: equal; M = 8:
+// 9.7 vs 9.4 with the delay).
 constexpr uint32_t kStreamDelay = 8;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -999,7 +1000,7 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream) {
   k.Pext = L.Pext;
   k.gext = L.gext;
   k.spin_limit = 1u << 20;   // ~0.5 s of polling: far beyond any healthy wait
-  k.stream_delay = ec_mode == 1 && L.M > 1 ? kStreamDelay : 0;
+  k.stream_delay = ec_mode == 1 && L.M > 4 ? kStreamDelay : 0;
   size_t lds = k.P > 0 ? sh.lds : 0;
   if (L.ec_mode && sh.lds_gemm > lds) lds = sh.lds_gemm;
   const bool exact = sh.CPS == 4 * sh.CPW && (int64_t)sh.CPS * sh.S == k.KC;
