@@ -13,9 +13,11 @@ last-level cache).  Timing uses HIP events on the stream the library launches
 on (torch's current stream).
 
 Also reported on the same line: per-token-count times and the EC overhead
-(same calls with the EC switched off), the prefill workload (M = 2048,
-K = 4096, N = 14336, rank 64) in TFLOP/s against the fp16 matrix-core peak,
-and the fp64 oracle timed on the host cores on a bounded sample.  Under
+(same calls with the EC switched off), the read rate a plain streaming read
+of the same bytes gets in one launch (the practical ceiling for a stream of
+this size), the prefill workload (M = 2048, K = 4096, N = 14336, rank 64) in
+TFLOP/s against the fp16 matrix-core peak, and the fp64 oracle timed on the
+host cores on a bounded sample (all threads, and one thread).  Under
 "mid_m", the mid-size token counts: the mixed-gate down_proj (M = 64 and
 512, K = 14336, N = 4096, rank 64; FUSED, SPLIT and EC off, skip threshold
 0 and 0.05; the FUSED/SPLIT crossover and the fraction of the binding
@@ -48,8 +50,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--pmc-mode", action="store_true",
-                    help="for hardware-counter runs: a few eager decode (M=16) and prefill calls and one "
-                         "plain device copy of 256 MiB (the counters' calibration), no timing line")
+                    help="for hardware-counter runs: a few eager decode calls (M=16), one plain device copy "
+                         "of 256 MiB and one streaming read of 64 MiB (the counters' calibrations), no timing line")
+    ap.add_argument("--pmc-prefill", action="store_true",
+                    help="for hardware-counter runs: a few eager prefill calls (fused, then EC off), no timing line")
     return ap.parse_args()
 
 
@@ -114,12 +118,15 @@ def time_calls(torch, calls, steps, warmup, graph=True):
     return start.elapsed_time(stop) / 1e3 / steps
 
 
-def make_call(sp, layer, M, b_g, variant, Ys, plans, workspace):
+def make_call(sp, layer, M, b_g, variant, Ys, plans, workspace, slot=0, stride=1):
+    """One call of the layer; call(i) reads weight copy (stride i + slot) mod R,
+    so the `stride` calls of one step (slots 0 .. stride-1) each read their own
+    copy and no call finds its weights in a cache."""
     plan = plans[(M, variant)]
     X = layer.X[:M]
 
     def call(i):
-        Wq, s, A, B, wg = layer.sets[i % len(layer.sets)]
+        Wq, s, A, B, wg = layer.sets[(stride * i + slot) % len(layer.sets)]
         if variant == "no_ec":
             A = B = wg = None
         sp.spear_w4ec_linear(X, Wq, s, A, B, wg, b_g, 0.0, variant, N=layer.N, plan=plan,
@@ -127,32 +134,84 @@ def make_call(sp, layer, M, b_g, variant, Ys, plans, workspace):
     return call
 
 
-def cpu_baseline(w, ms, budget_s):
-    """The oracle as it stands, on a bounded sample of the decode step."""
-    import numpy as np
+def _oracle_rate(w, ms, budget_s, W_deq):
+    """Decode steps of the oracle (the M of `ms` each) until `budget_s` passes:
+    (GB/s of algorithmic bytes, steps, seconds)."""
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()}))
-    except Exception:  # noqa: BLE001 - informational only
-        threads, blas = os.cpu_count() or 1, "?"
     Wq, s = oracle.pack_w4(w["W"])
     t0 = time.perf_counter()
     steps, nbytes = 0, 0
     while True:
         for M in ms:
-            oracle.w4ec_linear(w["X"][:M], Wq, s, w["A"], w["B"], w["w_g"], w["b_g"][M], K=w["K"], N=w["N"])
+            oracle.w4ec_linear(w["X"][:M], Wq, s, w["A"], w["B"], w["w_g"], w["b_g"][M], K=w["K"], N=w["N"],
+                               W_deq=W_deq)
             nbytes += workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"])
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    return nbytes / el / 1e9, steps, el
+
+
+def cpu_baseline(w, ms, budget_s):
+    """The oracle as it stands, on a bounded sample of the decode step: weight
+    preparation (quantize, pack, fp64 dequantization) timed once and apart;
+    then calls on the prepared weight with every BLAS thread, and with one
+    thread for the decode step and the tiny workload."""
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info()}))
+    t0 = time.perf_counter()
+    Wq, s = oracle.pack_w4(w["W"])
+    W_deq = oracle.dequant(Wq, s, w["K"], w["N"])
+    prep_s = time.perf_counter() - t0
+    rate, steps, el = _oracle_rate(w, ms, budget_s, W_deq)
+    one = {}
+    with threadpool_limits(limits=1):
+        r1, st1, el1 = _oracle_rate(w, ms, max(2.0, budget_s / 4), W_deq)
+        one["decode_q_proj_4096"] = {"GB/s": round(r1, 4), "steps": st1, "s": round(el1, 2)}
+        tiny = workloads.workload(1)
+        tq, ts = oracle.pack_w4(tiny["W"])
+        tW = oracle.dequant(tq, ts, tiny["K"], tiny["N"])
+        t1, n1 = time.perf_counter(), 0
+        while time.perf_counter() - t1 < 1.0:
+            oracle.w4ec_linear(tiny["X"], tq, ts, tiny["A"], tiny["B"], tiny["w_g"], tiny["b_g"][16],
+                               K=tiny["K"], N=tiny["N"], W_deq=tW)
+            n1 += 1
+        tel = time.perf_counter() - t1
+        one["tiny_16x512x512"] = {"us_per_call": round(tel / n1 * 1e6, 1), "calls": n1,
+                                  "GB/s": round(n1 * workloads.algorithmic_bytes(16, 512, 512, 16) / tel / 1e9, 4)}
+    return {"value": round(rate, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
-            "sample": f"{steps} decode step(s) (M=1,4,16 on K=N=4096, r=32), numpy float64 oracle incl. "
-                      f"dequantizing the packed weight each call, {el:.1f} s"}
+            "weight_prep_s": round(prep_s, 3),
+            "single_thread": one,
+            "sample": f"{steps} decode step(s) (M=1,4,16 on K=N=4096, r=32) of the numpy float64 oracle on its "
+                      f"dequantized weight (prepared once, {prep_s:.2f} s, not in the rate), {el:.1f} s"}
+
+
+def read_ceiling(torch, sp, nbytes, steps, graph):
+    """Best rate of a plain streaming read of `nbytes` bytes per launch
+    (spear_debug_stream_read), cold: each launch reads another copy of
+    R x nbytes >= 512 MiB, launches back to back (graph replay) as the layer's
+    calls are timed.  Returns (GB/s, grid, us per launch)."""
+    nb = -(-nbytes // 256) * 256
+    copies = max(2, -(-COLD_BYTES // nb))
+    buf = torch.ones(copies * nb // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
+    best = None
+    for grid in (256, 512, 1024, 2048):
+        def call(i, grid=grid):
+            off = (i % copies) * (nb // 4)
+            sp.spear_debug_stream_read(buf[off: off + nbytes // 4], grid, sink)
+        t = time_calls(torch, [call], steps, 5, graph)
+        rate = nbytes / t / 1e9
+        if best is None or rate > best[0]:
+            best = (rate, grid, t * 1e6)
+    del buf
+    return best
 
 
 PMC_COPY_BYTES = 256 << 20
@@ -186,6 +245,29 @@ def stored_traffic():
     return rec.get("bytes_per_launch")
 
 
+def pmc_prefill(torch, sp, workloads):
+    """Eager prefill calls for rocprofv3 --pmc runs: 6 fused, then 6 with the
+    EC off (each dispatch reported apart)."""
+    wp = workloads.workload(3)
+    pre = Layer(torch, sp, wp, 2)
+    Ys = [torch.empty((2048, wp["N"]), dtype=torch.float16, device="cuda:0")]
+    plans = {(2048, "auto"): sp.spear_dispatch_plan(2048, wp["K"], wp["N"], wp["r"], 0.0, 0.0, "auto"),
+             (2048, "no_ec"): sp.spear_dispatch_plan(2048, wp["K"], wp["N"], 0, 0.0, 0.0, "no_ec")}
+    ws = torch.zeros(max(max(p.workspace_bytes for p in plans.values()), 1 << 20), dtype=torch.uint8,
+                     device="cuda:0")
+    for v in ("auto", "no_ec"):
+        call = make_call(sp, pre, 2048, 0.0, v, Ys, plans, ws)
+        for i in range(6):
+            call(i)
+        torch.cuda.synchronize()
+    main_f, ec_f = workloads.algorithmic_flops(2048, wp["K"], wp["N"], wp["r"])
+    print(json.dumps({"pmc_prefill": True, "calls": 6, "main_flops": main_f, "ec_flops": ec_f,
+                      "source_digest": source_digest()}), flush=True)
+
+
+PMC_READ_BYTES = 64 << 20
+
+
 def pmc_mode(torch, sp, workloads):
     """Eager calls for rocprofv3 --pmc runs (each dispatch reported apart)."""
     w = workloads.workload(2)
@@ -202,8 +284,11 @@ def pmc_mode(torch, sp, workloads):
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda:0")
+    sp.spear_debug_stream_read(dst[: PMC_READ_BYTES // 2], 1024, sink)
+    torch.cuda.synchronize()
     print(json.dumps({"pmc_mode": True, "decode_calls": 8, "copy_bytes": PMC_COPY_BYTES,
-                      "source_digest": source_digest()}), flush=True)
+                      "stream_read_bytes": PMC_READ_BYTES, "source_digest": source_digest()}), flush=True)
 
 
 def main():
@@ -224,6 +309,9 @@ def main():
     if args.pmc_mode:
         pmc_mode(torch, sp, workloads)
         return
+    if args.pmc_prefill:
+        pmc_prefill(torch, sp, workloads)
+        return
 
     # ------------------------------------------------------------ decode
     w = workloads.workload(2)
@@ -241,7 +329,8 @@ def main():
     ws_bytes = max(p.workspace_bytes for p in plans.values())
     ws = torch.zeros(max(ws_bytes, 1 << 20), dtype=torch.uint8, device="cuda:0")
     graph = not args.eager
-    step_calls = [make_call(sp, dec, M, w["b_g"][M], "auto", Ys, plans, ws) for M in ms]
+    step_calls = [make_call(sp, dec, M, w["b_g"][M], "auto", Ys, plans, ws, slot=j, stride=len(ms))
+                  for j, M in enumerate(ms)]
     t_step = time_calls(torch, step_calls, args.steps, args.warmup, graph)
     step_bytes = sum(workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"]) for M in ms)
     value = step_bytes / t_step / 1e9
@@ -262,12 +351,17 @@ def main():
     dom_m = "16"
     b16 = workloads.algorithmic_bytes(16, w["K"], w["N"], w["r"])
     achieved = b16 / (per_m[dom_m]["us"] * 1e-6) / 1e9
+    del dec
+    ceil_rate, ceil_grid, ceil_us = read_ceiling(torch, sp, b16 // 16 * 16, args.steps, graph)
+    log(f"read ceiling for {b16 // 16 * 16} B per launch: {ceil_rate:.0f} GB/s ({ceil_us:.2f} us, grid {ceil_grid})")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
                 "kernel": "skinny_kernel (fused decode call at M=16, one launch per call)",
                 "bytes_per_launch": b16,
-                "launch_us": per_m[dom_m]["us"]}
-    del dec
+                "launch_us": per_m[dom_m]["us"],
+                "read_ceiling": {"GB/s": round(ceil_rate, 1), "us": round(ceil_us, 3), "grid": ceil_grid,
+                                 "what": "plain streaming read of the same bytes per launch, cold, back to back"},
+                "frac_of_read_ceiling": round(achieved / ceil_rate, 4)}
 
     # ------------------------------------------------------------ prefill
     prefill = None

@@ -25,7 +25,9 @@
  *     Faults inside kernels surface at the caller's next synchronization.
  *   - Row-major layouts; "fp16" is IEEE binary16.
  *   - No C++ exception crosses this interface.  Functions are reentrant; the
- *     only global state is a per-device cache of the compute-unit count.
+ *     global state is a per-device cache of the compute-unit count, a record
+ *     of which kernels had their LDS limit raised on which device, and the
+ *     debug bound of cross-workgroup waits (spear_debug_set_spin_limit).
  */
 #ifndef SPEAR_W4EC_H
 #define SPEAR_W4EC_H
@@ -149,6 +151,9 @@ spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t
 
 /*
  * spear_w4ec_linear -- Y = X . dequant(Wq, s) + g' (.) ((X . A) . B).
+ * SPEAR page, abstract: the low-bit GEMM of a layer whose quantization error
+ * is compensated by a small branch that a per-token gate scales, with the
+ * work after the branch's projection fused into that GEMM.
  *   desc     the call; plan may be NULL (planned internally) or the result of
  *            spear_dispatch_plan for the same M, K, N, rank and variant.
  *   X        fp16 [M, K], 16-byte aligned.
@@ -173,6 +178,12 @@ spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t
  *            workspace.
  * Errors: NULL_POINTER, INVALID_SHAPE, INVALID_ARGUMENT, MISALIGNED,
  *         WORKSPACE_TOO_SMALL, INVALID_PLAN, UNSUPPORTED, HIP.
+ * Device-side failure: the fused variants wait, inside the launch, for the
+ * EC projection that other workgroups of the same launch publish.  Every such
+ * wait is bounded; one that gives up (it never should: the bound is about
+ * half a second of polling) lets the call finish with a wrong Y and sets a
+ * bit of a sticky error word in the workspace header, which only
+ * spear_take_error reads and clears.
  */
 spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_plan_t* plan,
                                  const void* X, const void* Wq, const void* scales,
@@ -181,7 +192,9 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
 
 /*
  * spear_ec_project -- the EC projection and gate alone, in one pass over X
- * (the first half of the split variant):
+ * (the first half of the split variant).  SPEAR page, abstract: the error
+ * compensators are lightweight branches whose output a per-token gate
+ * scales; the branch's first factor and the gate read the same input.
  *   P[m, j] = sum_k X[m,k] A[k,j]   (fp32 [M, rank])
  *   g[m]    = g'(sigmoid(sum_k X[m,k] w_g[k] + b_g))   (fp32 [M], after tau)
  * X fp16 [M, K] 16-byte aligned; A fp16 [K, rank]; w_g fp16 [K]; rank >= 1.
@@ -193,6 +206,51 @@ spear_status_t spear_ec_workspace_bytes(int32_t M, int32_t K, int32_t rank, size
 spear_status_t spear_ec_project(int32_t M, int32_t K, int32_t rank, const void* X, const void* A,
                                 const void* w_g, float gate_bias, float skip_tau, void* P,
                                 void* g, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spear_take_error -- read and clear the sticky error word of a workspace.
+ * Enqueues on `stream` a kernel that writes the word to *code_out (device
+ * memory, uint32, 4-byte aligned) and sets it to zero, so the caller reads it
+ * after synchronizing the stream.  0: no wait gave up since the word was last
+ * cleared.  Bit 0 (1): a fused decode call's wait for the EC producers' hand-off
+ * gave up; bit 1 (2): a fused tiled call's wait for an EC row tile's ready
+ * flag gave up.  Each set bit means at least one call on this workspace wrote
+ * a wrong Y.  Ordered on `stream` like the calls it reports on.
+ * workspace and workspace_bytes as passed to spear_w4ec_linear (at least the
+ * 256 KiB header).
+ * Errors: NULL_POINTER, WORKSPACE_TOO_SMALL, MISALIGNED, HIP.
+ */
+spear_status_t spear_take_error(void* workspace, size_t workspace_bytes, void* code_out, void* stream);
+
+/*
+ * spear_debug_set_spin_limit -- bound of every cross-workgroup wait of later
+ * calls, in polls (process-wide; negative restores the default of 2^20).
+ * 0 makes a wait give up at its first unsuccessful poll: a test hook that
+ * lets the failure path run with every kernel still ending normally.
+ */
+void spear_debug_set_spin_limit(int64_t polls);
+
+/*
+ * spear_debug_fail_waits -- test hook (process-wide): while `on` is nonzero,
+ * every cross-workgroup wait of later fused calls looks for a tag that no
+ * workgroup writes, so it runs to its bound (spear_debug_set_spin_limit) and
+ * gives up; the kernels still end normally, Y is wrong and the sticky error
+ * word is set.  0 restores normal calls.
+ */
+void spear_debug_fail_waits(int32_t on);
+
+/*
+ * spear_debug_stream_read -- a plain streaming read of `bytes` bytes at src
+ * (16-byte loads, `grid` workgroups of 256 threads, each reading one
+ * contiguous share), with nothing computed but a fold of the loaded words; a
+ * measurement aid: the read rate one launch of a given size gets from the
+ * memory system, the practical ceiling of the weight stream of a decode call.
+ * src 16-byte aligned, bytes a multiple of 16; sink: device memory of `grid`
+ * uint32 (written only in the practically impossible case that a fold equals
+ * a magic value).
+ * Errors: NULL_POINTER, INVALID_SHAPE, MISALIGNED, HIP.
+ */
+spear_status_t spear_debug_stream_read(const void* src, size_t bytes, int32_t grid, void* sink, void* stream);
 
 /*
  * spear_debug_unpack_w4 -- decode a packed weight back to int8 codes

@@ -26,6 +26,10 @@ Pins (tests marked ``not gpu``):
   * scale/quantize: exhaustive fp16 check that the fp32 decisions equal the
     fp64 ones; |w - q s| <= s/2; grid weights w = s q quantize back to q;
     zero and subnormal-scale columns.
+  * group-wise scales (g128): one group spanning K reproduces the per-channel
+    quantizer bit for bit; a brute-force per-element loop; the s/2 bound and
+    grid weights per group; a group of zeros; the layer at g = 0 against the
+    textbook matmul with the group-dequantized weight.
   * gate: closed forms (g(0) = 1/2, g(-z) = 1 - g(z)), saturation at +-1e4,
     agreement with scipy.special.expit.
   * layer: g = 0 reduces to the textbook W4 GEMM; g = 1 reduces to a static
@@ -56,6 +60,10 @@ from .spear_oracle import (  # noqa: F401
     pack_w4,
     unpack_w4,
     dequant,
+    group_scales,
+    quantize_grouped,
+    pack_w4_grouped,
+    dequant_grouped,
     gate_logits,
     gate,
     ec_project,

@@ -185,6 +185,58 @@ def dequant(Wq, s, K, N):
 
 
 # --------------------------------------------------------------------------
+# Group-wise quantizer (the W4 variant next to per-channel scales).  The
+# abstract calls per-channel quantization the challenging setting, which
+# places it against the usual alternative, one scale per group of input rows
+# of each column.  Reading: groups of `group` consecutive k (128 here, the
+# common choice, and the k extent of one packed tile), the last group possibly
+# shorter; s[g, n] = fp16(max_{k in group g} |W[k, n]| / 7) and
+# q[k, n] = clamp(rint(W[k, n] / s[k // group, n]), -7, 7), q = 0 where the
+# group's s = 0; the same fp32 decisions as the per-channel quantizer, one
+# group at a time.  The codes are packed exactly as in layout 2; only the
+# scales change shape, to [ceil(K / group), N].
+# --------------------------------------------------------------------------
+
+def group_scales(W, group):
+    """fp16 scales s [ceil(K / group), N] of W [K, N] fp16, one per group of
+    `group` consecutive rows and column."""
+    W = np.asarray(W, dtype=np.float16)
+    K, N = W.shape
+    G = -(-K // group)
+    out = np.empty((G, N), dtype=np.float16)
+    for g in range(G):
+        out[g] = channel_scales(W[g * group: (g + 1) * group])
+    return out
+
+
+def quantize_grouped(W, s, group):
+    """int8 codes q [K, N] of W [K, N] under group scales s [ceil(K/group), N]."""
+    W = np.asarray(W, dtype=np.float16)
+    K, N = W.shape
+    q = np.empty((K, N), dtype=np.int8)
+    for g in range(np.asarray(s).shape[0]):
+        q[g * group: (g + 1) * group] = quantize(W[g * group: (g + 1) * group], np.asarray(s)[g])
+    return q
+
+
+def pack_w4_grouped(W, group=128):
+    """W [K, N] fp16 -> (Wq flat uint32 in layout 2, s [ceil(K/group), N] fp16)."""
+    W = np.asarray(W, dtype=np.float16)
+    K, N = W.shape
+    s = group_scales(W, group)
+    q = quantize_grouped(W, s, group)
+    return tile_words(pack_canonical(q), K, N), s
+
+
+def dequant_grouped(Wq, s, K, N, group):
+    """q * s[k // group, n] [K, N] float64, exact."""
+    q = unpack_w4(Wq, K, N).astype(np.float64)
+    s64 = np.asarray(s, dtype=np.float16).astype(np.float64)
+    rows = np.arange(K) // group
+    return q * s64[rows, :]
+
+
+# --------------------------------------------------------------------------
 # Gate.  Abstract: ECs "modulated by per-token gates".  Reading: one scalar
 # per token, g = sigmoid(X . w_g + b_g), from the layer's own fp16 input.
 # Optional skip threshold tau: g' = g if g >= tau else 0 (tau = 0: g' = g).
@@ -226,20 +278,27 @@ def ec_project(X, A, w_g, b_g):
     return P, gate_logits(X, w_g, b_g)
 
 
-def w4ec_linear(X, Wq, s, A, B, w_g, b_g, tau=0.0, K=None, N=None, gate_override=None):
+def w4ec_linear(X, Wq, s, A, B, w_g, b_g, tau=0.0, K=None, N=None, gate_override=None, W_deq=None,
+                group=None):
     """Y [M, N] float64 (unrounded) of the gated W4+EC linear layer.
 
-    Y = (X q) diag(s) + diag(g') (X A) B.  With rank 0 (A or B None or r = 0)
-    the EC term is absent.  `gate_override` replaces g' (tests only).
+    Y = X dequant(Wq, s) + diag(g') (X A) B, where dequant is q diag(s) for
+    per-channel scales s [N] (group None) and q * s[k // group, n] for group
+    scales s [ceil(K/group), N].  With rank 0 (A or B None or r = 0) the EC
+    term is absent.  `gate_override` replaces g' (tests only).  `W_deq`, if
+    given, must be that dequantized weight computed beforehand (the weight
+    preparation done once per weight); it is used as the product.
     Returns (Y, info) with info = {"z", "g", "g_eff", "ambiguous", "P"}.
     """
     X = np.asarray(X, dtype=np.float16)
     M, Kx = X.shape
     K = Kx if K is None else K
     if N is None:
-        N = np.asarray(s).shape[0]
+        N = np.asarray(s).shape[-1]
     X64 = X.astype(np.float64)
-    Y = X64 @ dequant(Wq, s, K, N)
+    if W_deq is None:
+        W_deq = dequant(Wq, s, K, N) if group is None else dequant_grouped(Wq, s, K, N, group)
+    Y = X64 @ W_deq
     info = {"z": None, "g": None, "g_eff": None, "ambiguous": np.zeros(M, bool), "P": None}
     r = 0 if (A is None or B is None) else np.asarray(A).shape[1]
     if r > 0:

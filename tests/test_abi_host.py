@@ -47,6 +47,24 @@ def test_status_strings_and_version(lib):
     assert lib.spear_status_str(99).decode() == "SPEAR_ERR_UNKNOWN"
 
 
+def test_service_entry_points_check_arguments(lib):
+    out = ctypes.c_uint32(0)
+    buf = ctypes.create_string_buffer(64)
+    # spear_take_error: null pointers, a workspace smaller than the header
+    assert lib.spear_take_error(None, 1 << 20, ctypes.byref(out), None) == 1
+    assert lib.spear_take_error(buf, 1 << 20, None, None) == 1
+    assert lib.spear_take_error(buf, 1024, ctypes.byref(out), None) == 5
+    # spear_debug_stream_read: shapes and alignment, before any launch
+    assert lib.spear_debug_stream_read(None, 64, 1, buf, None) == 1
+    assert lib.spear_debug_stream_read(buf, 0, 1, buf, None) == 2
+    assert lib.spear_debug_stream_read(buf, 24, 1, buf, None) == 2
+    assert lib.spear_debug_stream_read(buf, 64, 0, buf, None) == 2
+    # the debug knobs take any value and return nothing
+    lib.spear_debug_set_spin_limit(0)
+    lib.spear_debug_set_spin_limit(-1)
+    lib.spear_debug_fail_waits(0)
+
+
 def test_packed_bytes(lib):
     out = ctypes.c_size_t(0)
     assert lib.spear_packed_bytes(4096, 4096, ctypes.byref(out)) == 0 and out.value == 4096 * 4096 // 2

@@ -1,9 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
 Bar: packing and decoding bit-exact; outputs within relative L2 <= 1e-3 and
-max-abs <= 1e-2 rms(Y) of the unrounded fp64 result.  Full-size workloads are
-checked on sampled rows (each output row depends only on its own input row),
-small shapes element by element.  Oracle inputs come from the seeded
+max-abs <= 1e-2 rms(Y) of the unrounded fp64 result, over every element of Y
+(the full-size workloads included).  Oracle inputs come from the seeded
 generators and the oracle's own packing; nothing expected comes from the GPU.
 """
 import numpy as np
@@ -36,8 +35,23 @@ def run_linear(X, Wq_d, s_d, A, B, w_g, b_g, tau=0.0, variant="auto", N=None):
     return Y.cpu().numpy()
 
 
-def compare(Y_gpu, X, Wq_o, s_o, A, B, w_g, b_g, tau, K, N, where):
-    Y_ref, info = oracle.w4ec_linear(X, Wq_o, s_o, A, B, w_g, b_g, tau, K=K, N=N)
+_ORACLE_CACHE = {}
+
+
+def oracle_result(key, X, Wq_o, s_o, A, B, w_g, b_g, tau, K, N):
+    """oracle.w4ec_linear, memoized on `key` (None: not memoized) so the
+    variants of one full-size workload share one fp64 evaluation."""
+    if key is not None and key in _ORACLE_CACHE:
+        return _ORACLE_CACHE[key]
+    res = oracle.w4ec_linear(X, Wq_o, s_o, A, B, w_g, b_g, tau, K=K, N=N)
+    if key is not None:
+        _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[key] = res
+    return res
+
+
+def compare(Y_gpu, X, Wq_o, s_o, A, B, w_g, b_g, tau, K, N, where, key=None):
+    Y_ref, info = oracle_result(key, X, Wq_o, s_o, A, B, w_g, b_g, tau, K, N)
     amb = info["ambiguous"]
     Yg = Y_gpu.astype(np.float64)
     if amb.any():
@@ -121,14 +135,14 @@ def test_ec_project(M, K, r, b_g):
 
 # ----------------------------------------------------------------- layer
 
-def layer_case(X, W, A, B, w_g, b_g, tau, variant, where, rows=None):
+def layer_case(X, W, A, B, w_g, b_g, tau, variant, where, key=None):
+    """Every element of Y against the oracle; `key` memoizes the oracle's
+    result across the variants of one workload."""
     K, N = W.shape
     Wq_o, s_o = oracle.pack_w4(W)
     Wq_d, s_d = sp.spear_pack_w4(cuda(W))
     Y = run_linear(X, Wq_d, s_d, A, B, w_g, b_g, tau, variant, N=N)
-    if rows is not None:
-        return compare(Y[rows], X[rows], Wq_o, s_o, A, B, w_g, b_g, tau, K, N, where)
-    return compare(Y, X, Wq_o, s_o, A, B, w_g, b_g, tau, K, N, where)
+    return compare(Y, X, Wq_o, s_o, A, B, w_g, b_g, tau, K, N, where, key=key)
 
 
 @pytest.mark.parametrize("variant", ["auto", "split", "no_ec"])
@@ -144,30 +158,52 @@ def test_decode_workload(M):
     layer_case(w["X"][:M], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][M], 0.0, "auto", f"decode M={M}")
 
 
-@pytest.mark.parametrize("variant", ["auto", "split"])
-def test_prefill_workload_sampled_rows(variant):
+@pytest.mark.parametrize("variant", ["auto", "split", "no_ec"])
+def test_prefill_workload(variant):
+    """M = 2048, K = 4096, N = 14336, rank 64: every element of Y (the 256-row
+    tiles of the fused and split launches, and the W4 GEMM alone)."""
     w = workloads.workload(3)
-    rows = np.sort(np.random.default_rng(3).choice(2048, 48, replace=False))
-    rows = np.concatenate([[0, 1, 2047], rows])
-    layer_case(w["X"], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][2048], 0.0, variant,
-               f"prefill M=2048 {variant} (51 sampled rows)", rows=rows)
+    A, B, w_g = (w["A"], w["B"], w["w_g"]) if variant != "no_ec" else (None, None, None)
+    layer_case(w["X"], w["W"], A, B, w_g, w["b_g"][2048], 0.0, variant,
+               f"prefill M=2048 {variant} (all rows)", key=("prefill", variant == "no_ec"))
 
 
 @pytest.mark.parametrize("variant", ["fused", "split"])
 @pytest.mark.parametrize("M,tau", [(64, 0.0), (64, 0.05), (512, 0.0), (512, 0.05)])
 def test_mixed_gate_workload(M, tau, variant):
     w = workloads.workload(4)
-    rows = None if M == 64 else np.sort(np.random.default_rng(4).choice(M, 96, replace=False))
     layer_case(w["X"][:M], w["W"], w["A"], w["B"], w["w_g"], w["b_g"][M], tau, variant,
-               f"mixed-gate M={M} tau={tau} {variant}", rows=rows)
+               f"mixed-gate M={M} tau={tau} {variant}", key=("mixed", M, tau))
+
+
+@pytest.mark.parametrize("M", [64, 512])
+def test_mixed_gate_skip_deviation_from_exact(M):
+    """The skip threshold 0.05 departs from the exact definition (tau = 0) by
+    dropping the EC term of tokens with g < 0.05; report that departure for
+    the GPU output and the fp64 oracle (a report, not a parity bar: parity at
+    tau = 0.05 is against the tau-oracle above)."""
+    w = workloads.workload(4)
+    X = w["X"][:M]
+    K, N = w["W"].shape
+    Wq_o, s_o = oracle.pack_w4(w["W"])
+    Wq_d, s_d = sp.spear_pack_w4(cuda(w["W"]))
+    Y = run_linear(X, Wq_d, s_d, w["A"], w["B"], w["w_g"], w["b_g"][M], 0.05, "auto", N=N)
+    exact, _ = oracle.w4ec_linear(X, Wq_o, s_o, w["A"], w["B"], w["w_g"], w["b_g"][M], 0.0, K=K, N=N)
+    skip, info = oracle.w4ec_linear(X, Wq_o, s_o, w["A"], w["B"], w["w_g"], w["b_g"][M], 0.05, K=K, N=N)
+    dropped = int(np.sum((info["g"] > 0) & (info["g_eff"] == 0)))
+    rl_o, ma_o = oracle.rel_l2(skip, exact), oracle.max_abs_over_rms(skip, exact)
+    rl_g, ma_g = oracle.rel_l2(Y.astype(np.float64), exact), oracle.max_abs_over_rms(Y.astype(np.float64), exact)
+    note(f"mixed-gate M={M}: tau=0.05 drops the EC term of {dropped}/{M} tokens; deviation from the exact "
+         f"definition: oracle relL2={rl_o:.3e} maxabs/rms={ma_o:.3e}, GPU relL2={rl_g:.3e} maxabs/rms={ma_g:.3e}")
+    assert 0.6 * M <= dropped <= 0.8 * M
+    assert rl_g <= 1e-3
 
 
 @pytest.mark.parametrize("layer", range(7))
 def test_layer_stack(layer):
     lay = workloads.stack_layer(layer)
-    rows = np.sort(np.random.default_rng(layer).choice(256, 64, replace=False))
     layer_case(lay["X"], lay["W"], lay["A"], lay["B"], lay["w_g"], 0.0, 0.0, "auto",
-               f"stack {lay['name']}", rows=rows)
+               f"stack {lay['name']} (all rows)")
 
 
 @pytest.mark.parametrize("M,K,N,r", [(3, 136, 20, 5), (1, 8, 1, 1), (17, 264, 40, 3), (33, 512, 48, 256),
@@ -224,13 +260,11 @@ def test_tiled_ragged_shapes(M, K, N, r, variant):
 def test_large_tile_ragged_shapes(M, K, N, r, variant):
     """The 256-row tiles (256 x 256 and 256 x 224) on a partial last row
     tile, a K tail, a partial last column tile and a partial 32-column group;
-    sampled rows, the last rows included."""
+    every element of Y."""
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=7 * M + K + N + r, outliers=True)
     if variant == "no_ec":
         A = B = w_g = None
-    rows = np.sort(np.random.default_rng(M).choice(M, 40, replace=False))
-    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1], rows]))
-    layer_case(X, W, A, B, w_g, -0.5, 0.0, variant, f"large-tile {variant} M={M} K={K} N={N} r={r}", rows=rows)
+    layer_case(X, W, A, B, w_g, -0.5, 0.0, variant, f"large-tile {variant} M={M} K={K} N={N} r={r}")
 
 
 def test_empty_batch():
@@ -251,6 +285,31 @@ def test_identity_input_is_exact_dequant():
     I = np.eye(K, dtype=np.float16)
     Y = run_linear(I, Wq_d, s_d, None, None, None, 0.0, N=N)
     expect = oracle.dequant(Wq_o, s_o, K, N).astype(np.float16)
+    assert np.array_equal(Y.astype(np.float64), expect.astype(np.float64))
+
+
+@pytest.mark.parametrize("variant", ["no_ec", "fused", "split"])
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 4096), (1, 4096, 4096), (9, 14336, 4096), (16, 1000, 100)])
+def test_decode_identity_input_is_exact_dequant(M, K, N, variant):
+    """The decode (skinny) kernel's in-register int4 decode, bit for bit: X has
+    one-hot rows at k = k_i spread over K (first, last and interior chunks),
+    so Y[i, n] = fp16(s[n] q[k_i, n]) exactly (an 11-bit scale times a 4-bit
+    code is exact in fp32); with the EC on, b_g = -1e4 makes every gate 0, so
+    the fused and split variants must give the same bits."""
+    X0, W, A, B, w_g = workloads.random_layer(M, K, N, 32, seed=M + K + N)
+    ks = np.unique(np.concatenate([[0, K - 1], np.linspace(1, K - 2, max(M - 2, 0)).astype(int)]))[:M]
+    ks = np.resize(ks, M)
+    X = np.zeros((M, K), dtype=np.float16)
+    X[np.arange(M), ks] = 1.0
+    Wq_o, s_o = oracle.pack_w4(W)
+    Wq_d, s_d = sp.spear_pack_w4(cuda(W))
+    if variant == "no_ec":
+        A = B = w_g = None
+    p = sp.spear_dispatch_plan(M, K, N, 0 if A is None else 32, -1e4, variant=variant)
+    assert p.kernel == 0
+    Y = run_linear(X, Wq_d, s_d, A, B, w_g, -1e4, 0.0, variant, N=N)
+    expect = oracle.dequant(Wq_o, s_o, K, N)[ks].astype(np.float16)
+    note(f"decode identity {variant} M={M} K={K} N={N}: plan grid={p.grid} split_k={p.split_k} ec_local={p.ec_local}")
     assert np.array_equal(Y.astype(np.float64), expect.astype(np.float64))
 
 

@@ -24,6 +24,10 @@ __all__ = [
     "spear_ec_project",
     "spear_debug_unpack_w4",
     "spear_abi_version",
+    "spear_take_error",
+    "spear_debug_set_spin_limit",
+    "spear_debug_fail_waits",
+    "spear_debug_stream_read",
     "library",
     "SpearError",
 ]
@@ -175,3 +179,44 @@ def spear_ec_project(X, A, w_g, gate_bias, skip_tau=0.0):
                                     _stream(X.device))
     _binding.check(st, "spear_ec_project")
     return P, g
+
+
+def spear_take_error(workspace=None, device=None):
+    """Read and clear the sticky error word of a workspace (the cached one of
+    the current stream when None); synchronizes the current stream.  Returns
+    0, or the bits of the waits that gave up (1: fused decode hand-off, 2:
+    fused tiled ready flag)."""
+    if workspace is None:
+        dev = torch.device(device if device is not None else "cuda")
+        key = (dev.index if dev.index is not None else torch.cuda.current_device(),
+               torch.cuda.current_stream(dev).cuda_stream)
+        workspace = _workspaces.get(key)
+        if workspace is None:
+            return 0
+    _need(workspace, "workspace", torch.uint8, 1)
+    out = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+    st = library().spear_take_error(_ptr(workspace), workspace.numel(), _ptr(out), _stream(workspace.device))
+    _binding.check(st, "spear_take_error")
+    return int(out.item()) & 0xFFFFFFFF
+
+
+def spear_debug_set_spin_limit(polls):
+    """Bound of cross-workgroup waits in later calls (negative: the default)."""
+    library().spear_debug_set_spin_limit(int(polls))
+
+
+def spear_debug_fail_waits(on):
+    """Test hook: fused waits of later calls look for a tag nobody writes."""
+    library().spear_debug_fail_waits(1 if on else 0)
+
+
+def spear_debug_stream_read(src, grid, sink):
+    """Enqueue a plain streaming read of the bytes of `src` (a measurement aid)."""
+    _need(sink, "sink", torch.int32, 1)
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if sink.numel() < grid:
+        raise ValueError("sink needs one word per workgroup")
+    st = library().spear_debug_stream_read(_ptr(src), src.numel() * src.element_size(), int(grid), _ptr(sink),
+                                           _stream(src.device))
+    _binding.check(st, "spear_debug_stream_read")

@@ -37,6 +37,10 @@ EXPORTS = (
     "spear_ec_workspace_bytes",
     "spear_ec_project",
     "spear_debug_unpack_w4",
+    "spear_take_error",
+    "spear_debug_set_spin_limit",
+    "spear_debug_fail_waits",
+    "spear_debug_stream_read",
 )
 
 
@@ -104,6 +108,14 @@ def load(path=None):
     lib.spear_ec_project.argtypes = [i32, i32, i32, vp, vp, vp, f32, f32, vp, vp, vp, sz, vp]
     lib.spear_debug_unpack_w4.restype = ctypes.c_int
     lib.spear_debug_unpack_w4.argtypes = [vp, i32, i32, vp, vp]
+    lib.spear_take_error.restype = ctypes.c_int
+    lib.spear_take_error.argtypes = [vp, sz, vp, vp]
+    lib.spear_debug_set_spin_limit.restype = None
+    lib.spear_debug_set_spin_limit.argtypes = [ctypes.c_int64]
+    lib.spear_debug_fail_waits.restype = None
+    lib.spear_debug_fail_waits.argtypes = [ctypes.c_int32]
+    lib.spear_debug_stream_read.restype = ctypes.c_int
+    lib.spear_debug_stream_read.argtypes = [vp, sz, i32, vp, vp]
     if path == LIB_PATH:
         _lib = lib
     return lib

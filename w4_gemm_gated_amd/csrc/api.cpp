@@ -6,6 +6,9 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "internal.h"
 
@@ -15,6 +18,10 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_cache[kMaxDevices];
+// Polls before a cross-workgroup wait gives up (spear_debug_set_spin_limit).
+std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
+// Test hook (spear_debug_fail_waits): the fused waits look for tag ^ this.
+std::atomic<uint32_t> g_wait_xor{0};
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -55,6 +62,25 @@ bool same_plan(const spear_plan_t& a, const spear_plan_t& b) {
 spear_status_t hip_status(hipError_t e) { return e == hipSuccess ? SPEAR_OK : SPEAR_ERR_HIP; }
 
 }  // namespace
+
+namespace spear {
+
+// hipFuncSetAttribute applies to the current device: remember, per (kernel,
+// device), that it was set, so each device gets it once.
+hipError_t set_max_dynamic_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
+
+}  // namespace spear
 
 extern "C" {
 
@@ -198,6 +224,8 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
     s.workspace = workspace;
     s.Pext = ec_bytes ? (const float*)((const char*)workspace + L.p) : nullptr;
     s.gext = ec_bytes ? (const float*)((const char*)workspace + L.g) : nullptr;
+    s.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+    s.wait_xor = g_wait_xor.load(std::memory_order_relaxed);
     return hip_status(launch_skinny(s, stream));
   }
   GemmArgs ga;
@@ -214,7 +242,30 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
   }
   ga.fused = fused_tiled ? 1 : 0;
   ga.ecargs = e;
+  ga.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  ga.wait_xor = g_wait_xor.load(std::memory_order_relaxed);
   return hip_status(launch_gemm(ga, p, stream));
+}
+
+spear_status_t spear_take_error(void* workspace, size_t workspace_bytes, void* code_out, void* stream) {
+  if (!workspace || !code_out) return SPEAR_ERR_NULL_POINTER;
+  if (workspace_bytes < kSyncHeaderBytes) return SPEAR_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(workspace, 16) || !aligned(code_out, 4)) return SPEAR_ERR_MISALIGNED;
+  return hip_status(launch_take_error(workspace, code_out, stream));
+}
+
+void spear_debug_set_spin_limit(int64_t polls) {
+  const uint32_t v = polls < 0 ? kDefaultSpinLimit : polls > (int64_t)UINT32_MAX ? UINT32_MAX : (uint32_t)polls;
+  g_spin_limit.store(v, std::memory_order_relaxed);
+}
+
+void spear_debug_fail_waits(int32_t on) { g_wait_xor.store(on ? 0x40000000u : 0u, std::memory_order_relaxed); }
+
+spear_status_t spear_debug_stream_read(const void* src, size_t bytes, int32_t grid, void* sink, void* stream) {
+  if (!src || !sink) return SPEAR_ERR_NULL_POINTER;
+  if (bytes == 0 || bytes % 16 != 0 || grid < 1) return SPEAR_ERR_INVALID_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return SPEAR_ERR_MISALIGNED;
+  return hip_status(launch_stream_read(src, bytes, grid, sink, stream));
 }
 
 }  // extern "C"

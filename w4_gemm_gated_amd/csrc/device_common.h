@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace spear {
 
 typedef _Float16 half_t;
@@ -152,6 +154,52 @@ __device__ __forceinline__ void wait_vm_le() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t or_dev_u32(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Call epochs of the fused variants.  Every block of a fused call reads the
+// epoch word of the workspace header when it starts; the call's tag is
+// epoch + 1, the value that its ready flags and hand-off entries carry.  The
+// epoch stays in [0, 2^32 - 2], so a tag is never 0 (the value of a zero-filled
+// header).  Each block counts itself out once it no longer needs the tag
+// (count_out, run by one whole wave); the last of the call's blocks returns
+// the finisher count to zero and advances the epoch to the tag.  When the tag
+// is the largest value, that block instead clears every tagged word of the
+// header (the ready flags and the hand-off slabs) and restarts the epoch at 0,
+// so no word written before the wrap can match a later tag.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kLastTag = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint32_t call_tag(const uint32_t* sync) {
+  return ld_dev_u32(&sync[kSyncEpoch]) + 1u;
+}
+
+__device__ __noinline__ void count_out(uint32_t* sync, uint32_t total, uint32_t tag) {
+  const int lane = threadIdx.x % kWave;
+  uint32_t before = 0;
+  if (lane == 0) before = add_dev_u32(&sync[kSyncFinishers], 1u);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before != total - 1) return;
+  if (tag == kLastTag) {
+    unsigned char* base = reinterpret_cast<unsigned char*>(sync) - kGemmSyncOffset;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)kSyncHeaderBytes);
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    // ready flags: words [kEcReadyWord, 8192) of the EC counter region
+    for (uint32_t off = kEcReadyWord * 4u + 16u * lane; off < 8192u * 4u; off += 16u * kWave)
+      __builtin_amdgcn_raw_buffer_store_b128(z, r, off, 0, kCachePolicySc1);
+    for (uint32_t off = (uint32_t)kHandoffOffset + 16u * lane; off < (uint32_t)(kHandoffOffset + kHandoffBytes);
+         off += 16u * kWave)
+      __builtin_amdgcn_raw_buffer_store_b128(z, r, off, 0, kCachePolicySc1);
+    drain_vm();
+  }
+  if (lane == 0) {
+    st_dev_u32(&sync[kSyncFinishers], 0u);
+    st_dev_u32(&sync[kSyncEpoch], tag == kLastTag ? 0u : tag);
+  }
 }
 
 }  // namespace spear

@@ -54,9 +54,8 @@ __global__ void __launch_bounds__(kEcThreads) ec_project_kernel(EcKArgs a) {
 
 template <bool DMA, bool GVEC, int PB>
 hipError_t launch_ec_pb(const EcKArgs& a, dim3 grid, size_t lds, void* stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ec_project_kernel<DMA, GVEC, PB>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      96 * 1024);
+  const hipError_t attr =
+      set_max_dynamic_lds(reinterpret_cast<const void*>(&ec_project_kernel<DMA, GVEC, PB>), 96 * 1024);
   if (attr != hipSuccess) return attr;
   if (ec_kb_for(PB) * 32 != a.ss) return hipErrorInvalidValue;   // sub-slab and block count disagree
   hipLaunchKernelGGL((ec_project_kernel<DMA, GVEC, PB>), grid, dim3(kEcThreads), lds, (hipStream_t)stream, a);

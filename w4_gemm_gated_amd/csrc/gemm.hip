@@ -60,8 +60,9 @@ struct GemmKArgs {
   // Fused launch only: P and g are produced by the launch's EC workgroups.
   const uint32_t* ready;  // [ec row tiles of 64] flags, raised to the call's tag
   int ec_tiles;           // EC row tiles
-  uint32_t* error;        // set when a wait for a ready flag gives up
+  uint32_t* error;        // sticky error word: kErrReadyWait when a wait for a ready flag gives up
   uint32_t spin_limit;
+  uint32_t wait_xor;      // the tiles wait for tag ^ wait_xor (0, or a test hook's value)
 };
 
 // The fused launch: E EC workgroups (the first blocks), then the GEMM tiles.
@@ -111,12 +112,12 @@ __device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t 
 #pragma unroll
     for (int i = 0; i < (TM + 63) / 64; ++i) {
       const int t = m0 / 64 + i;
-      if (t >= t_end || early[i] == tag) continue;
+      if (t >= t_end || early[i] == (tag ^ a.wait_xor)) continue;
       uint32_t n = 0;
-      while (ld_dev_u32(&a.ready[t]) != tag) {
+      while (ld_dev_u32(&a.ready[t]) != (tag ^ a.wait_xor)) {
         __builtin_amdgcn_s_sleep(2);
         if (++n > a.spin_limit) {
-          st_dev_u32(a.error, 1u);
+          or_dev_u32(a.error, kErrReadyWait);
           break;
         }
       }
@@ -512,12 +513,12 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
 // indices, so they are dispatched before any GEMM workgroup and never wait
 // for one; a GEMM workgroup waits only in its epilogue, for ready flags that
 // the EC workgroups raise.  Every block reads the call epoch first and counts
-// itself out last; the last to finish returns the finisher count to zero and
-// advances the epoch (every block has read it by then).
+// itself out last (count_out: the last to finish returns the finisher count
+// to zero and advances the epoch; every block has read it by then).
 template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB>
 __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs f) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const uint32_t tag = ld_dev_u32(&f.sync[kSyncEpoch]) + 1u;
+  const uint32_t tag = call_tag(f.sync);
   const int b = blockIdx.x;
   if (b < f.E) {
     if (b < f.ec_blocks) ec_block<true, true, PB>(f.e, lds, b % f.e.m_tiles, b / f.e.m_tiles, tag);
@@ -525,21 +526,14 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs 
     gemm_block<MBW, NBW, WM, WN, SPLIT, true>(f.g, b - f.E, lds, tag);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t before = add_dev_u32(&f.sync[kSyncFinishers], 1u);
-    if (before == gridDim.x - 1) {
-      st_dev_u32(&f.sync[kSyncFinishers], 0u);
-      st_dev_u32(&f.sync[kSyncEpoch], tag);
-    }
-  }
+  if (threadIdx.x < kWave) count_out(f.sync, gridDim.x, tag);
 }
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT>
 hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
   constexpr size_t lds = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, stages_for(16 * MBW * WM, SPLIT)>();
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t attr =
+      set_max_dynamic_lds(reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>), (int)lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>), dim3((unsigned)(k.MT * k.NT * k.S)),
                      dim3(kGemmThreads), lds, (hipStream_t)stream, k);
@@ -552,9 +546,8 @@ hipError_t launch_fused_pb(const FusedKArgs& f, void* stream) {
   const size_t ec = ec_lds_bytes(f.e.ss, f.e.rp);
   const size_t lds = tile > ec ? tile : ec;
   if (ec_kb_for(PB) * 32 != f.e.ss || lds > kMaxLdsBytes - 1024) return hipErrorInvalidValue;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLdsBytes - 1024));
+  const hipError_t attr = set_max_dynamic_lds(
+      reinterpret_cast<const void*>(&w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB>), (int)(kMaxLdsBytes - 1024));
   if (attr != hipSuccess) return attr;
   const unsigned grid = (unsigned)(f.E + f.g.MT * f.g.NT * f.g.S);
   hipLaunchKernelGGL((w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB>), dim3(grid), dim3(kGemmThreads), lds,
@@ -644,7 +637,8 @@ hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream
   k.ready = nullptr;
   k.ec_tiles = 0;
   k.error = sync + kSyncError;
-  k.spin_limit = 1u << 20;   // ~0.5 s of polling: far beyond any healthy wait
+  k.spin_limit = a.spin_limit;
+  k.wait_xor = a.wait_xor;
   if (a.fused) {
     // EC workgroups first (P and g into the EC workspace, ready flags in the
     // EC counter region), then the GEMM tiles.

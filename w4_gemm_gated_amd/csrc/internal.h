@@ -43,6 +43,13 @@ constexpr int64_t kMaxSyncWords = 8192;   // per counter region
 // 128-byte line: fused finisher count, error flag, call epoch (advanced by
 // every fused call), then split-K tile counters.
 constexpr int kSyncFinishers = 32, kSyncError = 64, kSyncEpoch = 96, kSyncTiles = 128;
+// Bits of the sticky error word (kSyncError): a bounded wait gave up, so the
+// call that set it wrote a wrong Y.  spear_take_error reads and clears it.
+constexpr uint32_t kErrHandoffWait = 1u;   // fused decode: the producers' hand-off
+constexpr uint32_t kErrReadyWait = 2u;     // fused tiled: an EC row tile's ready flag
+// Default bound of every cross-workgroup wait, in polls (about half a second:
+// far beyond any healthy wait).
+constexpr uint32_t kDefaultSpinLimit = 1u << 20;
 // EC counter region ([0, 32 KiB)): row-tile counters in words [0, 4096), the
 // fused tiled launch's ready flags (raised to the call's epoch + 1) in words
 // [4096, 8192).
@@ -107,6 +114,8 @@ struct GemmArgs {
   size_t scratch_base; // first workspace byte the GEMM may use as scratch
   int32_t fused;       // P and g computed by EC workgroups of the same launch
   EcArgs ecargs;       // fused: the projection's arguments (P and g in the EC workspace)
+  uint32_t spin_limit; // polls before a cross-workgroup wait gives up
+  uint32_t wait_xor;   // 0; nonzero (test hook) makes every wait look for a tag nobody writes
 };
 
 // Skinny (M <= 16) kernel: tile shape, producers and workspace layout.
@@ -144,6 +153,8 @@ struct SkinnyLaunch {
   void* workspace;          // skinny workspace (layout in shape)
   const float* Pext;        // ec_mode 2
   const float* gext;
+  uint32_t spin_limit;      // polls before a cross-workgroup wait gives up
+  uint32_t wait_xor;        // 0; nonzero (test hook) makes every wait look for a tag nobody writes
 };
 hipError_t launch_skinny(const SkinnyLaunch& L, void* stream);
 
@@ -166,6 +177,11 @@ TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_
 // then cover less than two thirds of the GPU.
 TiledShape fused_tiled_shape(int64_t M, int64_t K, int64_t N, int cus, int ec_blocks, size_t scratch_base);
 
+// Raise a kernel's dynamic-LDS limit on the current device (once per kernel
+// and device; later calls return at once).
+hipError_t set_max_dynamic_lds(const void* kernel, int bytes);
+hipError_t launch_take_error(void* workspace, void* out, void* stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, int grid, void* sink, void* stream);
 hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);
 hipError_t launch_ec_project(const EcArgs& a, void* stream);

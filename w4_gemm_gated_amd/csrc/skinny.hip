@@ -25,8 +25,9 @@
 //     itself.
 // Data crosses workgroups only through device-coherent stores and loads (see
 // device_common.h), never through L2 write-backs.  Every call returns its
-// counters to zero and advances the epoch; the last GEMM workgroup to finish
-// does both, when every producer and every reader is done.
+// counters to zero and advances the epoch; the last of its workgroups
+// (producers included) to finish does both, when every producer has read the
+// call's tag and every reader is done.
 #include <algorithm>
 
 #include "device_common.h"
@@ -48,7 +49,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Sync words of the GEMM half of the counter header, each hot one on its own
 // 128-byte line (pollers and updaters of different words never share one).
-constexpr int kFinishers = kSyncFinishers, kError = kSyncError, kEpoch = kSyncEpoch, kTiles = kSyncTiles;
+constexpr int kError = kSyncError, kTiles = kSyncTiles;
 
 struct SkinnyKArgs {
   const half_t* X;
@@ -62,14 +63,15 @@ struct SkinnyKArgs {
   int T, S, CPS, P, ksp, ps, r1p;
   int ec_mode;            // 0: no EC; 1: fused producers; 2: P and g given (split variant)
   float gate_bias, skip_tau;
-  uint32_t* sync;         // [kFinishers] GEMM workgroups done, [kError] error, [kEpoch] call
-                          // epoch, [kTiles + t] split-K tile counters
+  uint32_t* sync;         // [kFinishers] workgroups done, [kError] sticky error bits, [kEpoch]
+                          // call epoch, [kTiles + t] split-K tile counters
   uint64_t* handoff;      // ec_mode 1: [P][M][r1p] slab sums of [P | z], each
                           // (epoch + 1) << 32 | float bits
   float* gemm_part;       // [T*S][NBW][64][4]
   const float* Pext;      // ec_mode 2: [M][ps]
   const float* gext;      // ec_mode 2: [M]
   uint32_t spin_limit;
+  uint32_t wait_xor;      // the consumers wait for tag ^ wait_xor (0, or a test hook's value)
   uint32_t stream_delay;  // ec_mode 1: s_sleep units before the weight stream (producers' head start)
 };
 
@@ -250,7 +252,7 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
   // k0*rank*2 is a multiple of 16) and the w_g slab; clamped units duplicate
   // the last real unit.  X rows >= M and k >= K read as zeros.
   if (w < kCopyWaves) {
-    if (w == 0) tag = ld_dev_u32(&a.sync[kEpoch]) + 1u;
+    if (w == 0) tag = call_tag(a.sync);
     const int nvec = kn * a.rank / 8;
     const u32x4_t* asrc = reinterpret_cast<const u32x4_t*>(a.A + (size_t)k0 * a.rank);
     for (int base = w * kWave; base < prod_a_units(ksp, a.rank); base += kCopyWaves * kWave)
@@ -274,6 +276,9 @@ __device__ void ec_producer(const SkinnyKArgs& a, unsigned char* lds, int p) {
   else if (kbw == 2) producer_passes<2>(a, L, p, w, tag);
   else if (kbw == 4) producer_passes<4>(a, L, p, w, tag);
   else producer_passes<8>(a, L, p, w, tag);
+  // Wave 0 read the tag; the epoch may move on only after every producer
+  // has (a later read would tag this call's slabs with the next call's tag).
+  if (w == 0) count_out(a.sync, (uint32_t)(a.T * a.S + a.P), tag);
 }
 
 // ---------------------------------------------------------------- local EC
@@ -481,7 +486,7 @@ __device__ __forceinline__ void handoff_wait(const SkinnyKArgs& a, __amdgpu_buff
       }
     if (!__any(stale)) break;
     if (n >= a.spin_limit) {
-      if (threadIdx.x % kWave == 0) st_dev_u32(&a.sync[kError], 1u);
+      if (threadIdx.x % kWave == 0) or_dev_u32(&a.sync[kError], kErrHandoffWait);
       break;
     }
     __builtin_amdgcn_s_sleep(4);
@@ -580,7 +585,7 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
   const int pcs = gemm_pc_stride(a.rank, a.ps);
   // The epoch is read before the weight stream is requested, so it returns
   // ahead of it.
-  const uint32_t tag = ECM == 1 ? ld_dev_u32(&a.sync[kEpoch]) + 1u : 0u;
+  const uint32_t tag = ECM == 1 ? call_tag(a.sync) : 0u;
 
   // ---- EC operands that are ready now, ahead of the weight stream: the B
   // tile (element q = row * TN + column; rows >= rank and columns >= N
@@ -743,13 +748,7 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
     }
     __syncthreads();
     if (!flags[1]) {
-      if (ECM == 1 && tid == 0) {
-        const uint32_t before = add_dev_u32(&a.sync[kFinishers], 1u);
-        if (before == (uint32_t)(a.T * a.S - 1)) {
-          st_dev_u32(&a.sync[kFinishers], 0u);
-          st_dev_u32(&a.sync[kEpoch], tag);
-        }
-      }
+      if (ECM == 1 && w == 0) count_out(a.sync, (uint32_t)(a.T * a.S + a.P), tag);
       return;
     }
     if (w == 0) {
@@ -772,19 +771,12 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
     // about when it is, normally just before the producers publish, which
     // costs a second round trip.)  Sixteen loads in flight per thread.
     const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.handoff, (uint32_t)((size_t)a.P * a.M * a.r1p * 8));
-    if (a.P <= 8) gather_handoff<2, 8>(a, hr, tag, Pc, pcs);
-    else gather_handoff<1, 16>(a, hr, tag, Pc, pcs);
+    if (a.P <= 8) gather_handoff<2, 8>(a, hr, tag ^ a.wait_xor, Pc, pcs);
+    else gather_handoff<1, 16>(a, hr, tag ^ a.wait_xor, Pc, pcs);
     __syncthreads();
-    // Count this workgroup out (wave 1, off wave 0's path): the last one
-    // returns the counters to zero and advances the epoch (every producer and
-    // every reader is done by then).
-    if (tid == kWave) {
-      const uint32_t before = add_dev_u32(&a.sync[kFinishers], 1u);
-      if (before == (uint32_t)(a.T * a.S - 1)) {
-        st_dev_u32(&a.sync[kFinishers], 0u);
-        st_dev_u32(&a.sync[kEpoch], tag);
-      }
-    }
+    // Count this workgroup out (wave 1, off wave 0's path): the last of the
+    // call's workgroups returns the counters to zero and advances the epoch.
+    if (w == 1) count_out(a.sync, (uint32_t)(a.T * a.S + a.P), tag);
   }
   if (w > 0) return;
 
@@ -833,13 +825,10 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
 }
 
 // Let a kernel use all of a workgroup's LDS beside its static LDS (once per
-// instantiation).
+// instantiation and device).
 template <auto Kernel, int NBW>
 hipError_t allow_full_lds() {
-  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  (int)(kMaxLdsBytes - static_lds_bytes(NBW)));
-  return e;
+  return set_max_dynamic_lds(reinterpret_cast<const void*>(Kernel), (int)(kMaxLdsBytes - static_lds_bytes(NBW)));
 }
 
 template <int NBW, int CPW, bool EXACT>
@@ -999,7 +988,8 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream) {
   k.gemm_part = (float*)(ws + sh.ws_gemm_part);
   k.Pext = L.Pext;
   k.gext = L.gext;
-  k.spin_limit = 1u << 20;   // ~0.5 s of polling: far beyond any healthy wait
+  k.spin_limit = L.spin_limit;
+  k.wait_xor = L.wait_xor;
   k.stream_delay = ec_mode == 1 && L.M > 4 ? kStreamDelay : 0;
   size_t lds = k.P > 0 ? sh.lds : 0;
   if (L.ec_mode && sh.lds_gemm > lds) lds = sh.lds_gemm;
