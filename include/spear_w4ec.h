@@ -191,6 +191,28 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spear_w4ec_linear_noalloc -- spear_w4ec_linear without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that forbid allocation).  Same arguments and result
+ * as spear_w4ec_linear minus workspace and workspace_bytes; it allocates
+ * nothing (no hipMalloc, no allocating library call).  Its workspace is the
+ * library's own device array of SPEAR_NOALLOC_WORKSPACE_BYTES (32 MiB) per GPU,
+ * kept until the process ends; its address is looked up on the first call on
+ * each device, which also enqueues on `stream` a small kernel that zeroes the
+ * array's 256 KiB header before the call.  Every call on one GPU shares that
+ * array: calls that overlap in time on one GPU race and must not be issued
+ * (order them, e.g. on one stream).  Its sticky error word is read with
+ * spear_take_error(NULL, 0, code_out, stream).
+ * Errors: as spear_w4ec_linear; WORKSPACE_TOO_SMALL when the plan needs more
+ * than SPEAR_NOALLOC_WORKSPACE_BYTES (nothing is enqueued then).
+ */
+#define SPEAR_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+spear_status_t spear_w4ec_linear_noalloc(const spear_linear_desc_t* desc, const spear_plan_t* plan,
+                                         const void* X, const void* Wq, const void* scales,
+                                         const void* A, const void* B, const void* w_g, void* Y,
+                                         void* stream);
+
+/*
  * spear_ec_project -- the EC projection and gate alone, in one pass over X
  * (the first half of the split variant).  SPEAR page, abstract: the error
  * compensators are lightweight branches whose output a per-token gate
@@ -217,7 +239,8 @@ spear_status_t spear_ec_project(int32_t M, int32_t K, int32_t rank, const void* 
  * flag gave up.  Each set bit means at least one call on this workspace wrote
  * a wrong Y.  Ordered on `stream` like the calls it reports on.
  * workspace and workspace_bytes as passed to spear_w4ec_linear (at least the
- * 256 KiB header).
+ * 256 KiB header); workspace NULL with workspace_bytes 0 reads the word of
+ * spear_w4ec_linear_noalloc's workspace on the current device.
  * Errors: NULL_POINTER, WORKSPACE_TOO_SMALL, MISALIGNED, HIP.
  */
 spear_status_t spear_take_error(void* workspace, size_t workspace_bytes, void* code_out, void* stream);

@@ -25,6 +25,7 @@ __all__ = [
     "spear_debug_unpack_w4",
     "spear_abi_version",
     "spear_take_error",
+    "spear_w4ec_linear_noalloc",
     "spear_debug_set_spin_limit",
     "spear_debug_fail_waits",
     "spear_debug_stream_read",
@@ -160,6 +161,48 @@ def spear_w4ec_linear(X, Wq, scales, A, B, w_g, gate_bias, skip_tau=0.0, variant
                                      _stream(X.device))
     _binding.check(st, "spear_w4ec_linear")
     return Y
+
+
+def spear_w4ec_linear_noalloc(X, Wq, scales, A, B, w_g, gate_bias, skip_tau=0.0, variant="auto", N=None,
+                              plan=None, Y=None):
+    """spear_w4ec_linear on the library's own device workspace (no workspace
+    argument; the library call allocates nothing).  Y is allocated here when
+    not given."""
+    _need(X, "X", torch.float16, 2)
+    _need(Wq, "Wq", torch.uint8, 1)
+    _need(scales, "scales", torch.float16, 1)
+    M, K = X.shape
+    N = scales.shape[0] if N is None else int(N)
+    rank = 0
+    if A is not None:
+        _need(A, "A", torch.float16, 2)
+        _need(B, "B", torch.float16, 2)
+        _need(w_g, "w_g", torch.float16, 1)
+        rank = A.shape[1]
+        if A.shape[0] != K or B.shape != (rank, N) or w_g.shape[0] != K:
+            raise ValueError("EC shapes must be A [K, r], B [r, N], w_g [K]")
+    if Wq.numel() != spear_packed_bytes(K, N):
+        raise ValueError("Wq size does not match K and N")
+    d = _desc(M, K, N, rank, gate_bias, skip_tau, variant, 0)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    else:
+        _need(Y, "Y", torch.float16, 2)
+    st = library().spear_w4ec_linear_noalloc(ctypes.byref(d), ctypes.byref(plan) if plan is not None else None,
+                                             _ptr(X), _ptr(Wq), _ptr(scales), _ptr(A), _ptr(B), _ptr(w_g),
+                                             _ptr(Y), _stream(X.device))
+    _binding.check(st, "spear_w4ec_linear_noalloc")
+    return Y
+
+
+def spear_take_error_noalloc(device=None):
+    """Read and clear the sticky error word of the allocation-free entry
+    point's workspace on the current device; synchronizes the stream."""
+    dev = torch.device(device if device is not None else "cuda")
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = library().spear_take_error(None, 0, _ptr(out), _stream(dev))
+    _binding.check(st, "spear_take_error")
+    return int(out.item()) & 0xFFFFFFFF
 
 
 def spear_ec_project(X, A, w_g, gate_bias, skip_tau=0.0):

@@ -38,6 +38,7 @@ EXPORTS = (
     "spear_ec_project",
     "spear_debug_unpack_w4",
     "spear_take_error",
+    "spear_w4ec_linear_noalloc",
     "spear_debug_set_spin_limit",
     "spear_debug_fail_waits",
     "spear_debug_stream_read",
@@ -108,6 +109,9 @@ def load(path=None):
     lib.spear_ec_project.argtypes = [i32, i32, i32, vp, vp, vp, f32, f32, vp, vp, vp, sz, vp]
     lib.spear_debug_unpack_w4.restype = ctypes.c_int
     lib.spear_debug_unpack_w4.argtypes = [vp, i32, i32, vp, vp]
+    lib.spear_w4ec_linear_noalloc.restype = ctypes.c_int
+    lib.spear_w4ec_linear_noalloc.argtypes = [ctypes.POINTER(LinearDesc), ctypes.POINTER(Plan),
+                                              vp, vp, vp, vp, vp, vp, vp, vp]
     lib.spear_take_error.restype = ctypes.c_int
     lib.spear_take_error.argtypes = [vp, sz, vp, vp]
     lib.spear_debug_set_spin_limit.restype = None

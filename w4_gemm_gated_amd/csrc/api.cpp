@@ -65,6 +65,23 @@ spear_status_t hip_status(hipError_t e) { return e == hipSuccess ? SPEAR_OK : SP
 
 namespace spear {
 
+spear_status_t resolve_plan(const spear_linear_desc_t& desc, const spear_plan_t* plan, spear_plan_t* out) {
+  spear_status_t st = check_desc(desc);
+  if (st != SPEAR_OK) return st;
+  if (!plan) return plan_for(desc, out);
+  if (plan->abi_version != SPEAR_ABI_VERSION || plan->layout_id != SPEAR_LAYOUT_ID) return SPEAR_ERR_INVALID_PLAN;
+  if (plan->variant < SPEAR_VARIANT_FUSED || plan->variant > SPEAR_VARIANT_NO_EC || plan->cus <= 0)
+    return SPEAR_ERR_INVALID_PLAN;
+  spear_linear_desc_t d2 = desc;
+  d2.variant = plan->variant;
+  d2.device_cus = plan->cus;
+  spear_plan_t again;
+  st = make_plan(d2, plan->cus, &again);
+  if (st != SPEAR_OK || !same_plan(again, *plan)) return SPEAR_ERR_INVALID_PLAN;
+  *out = *plan;
+  return SPEAR_OK;
+}
+
 // hipFuncSetAttribute applies to the current device: remember, per (kernel,
 // device), that it was set, so each device gets it once.
 hipError_t set_max_dynamic_lds(const void* kernel, int bytes) {
@@ -91,7 +108,7 @@ const char* spear_status_str(spear_status_t s) {
     case SPEAR_ERR_INVALID_SHAPE: return "SPEAR_ERR_INVALID_SHAPE: need M >= 0, K >= 8, K % 8 == 0, N >= 1, 0 <= rank <= 256";
     case SPEAR_ERR_UNSUPPORTED: return "SPEAR_ERR_UNSUPPORTED: request outside what the kernels implement";
     case SPEAR_ERR_MISALIGNED: return "SPEAR_ERR_MISALIGNED: X, Wq and workspace need 16-byte, fp16 tensors 2-byte alignment";
-    case SPEAR_ERR_WORKSPACE_TOO_SMALL: return "SPEAR_ERR_WORKSPACE_TOO_SMALL: workspace_bytes < plan.workspace_bytes";
+    case SPEAR_ERR_WORKSPACE_TOO_SMALL: return "SPEAR_ERR_WORKSPACE_TOO_SMALL: workspace_bytes < plan.workspace_bytes (spear_w4ec_linear_noalloc: the plan needs more than its 32 MiB)";
     case SPEAR_ERR_INVALID_PLAN: return "SPEAR_ERR_INVALID_PLAN: plan does not match the descriptor or this library";
     case SPEAR_ERR_HIP: return "SPEAR_ERR_HIP: the HIP runtime reported an error";
     case SPEAR_ERR_INVALID_ARGUMENT: return "SPEAR_ERR_INVALID_ARGUMENT: non-finite bias, tau outside [0, 1] or unknown variant";
@@ -163,25 +180,9 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
                                  const void* B, const void* w_g, void* Y, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   if (!desc) return SPEAR_ERR_NULL_POINTER;
-  spear_status_t st = check_desc(*desc);
-  if (st != SPEAR_OK) return st;
   spear_plan_t p;
-  if (plan) {
-    if (plan->abi_version != SPEAR_ABI_VERSION || plan->layout_id != SPEAR_LAYOUT_ID)
-      return SPEAR_ERR_INVALID_PLAN;
-    if (plan->variant < SPEAR_VARIANT_FUSED || plan->variant > SPEAR_VARIANT_NO_EC || plan->cus <= 0)
-      return SPEAR_ERR_INVALID_PLAN;
-    spear_linear_desc_t d2 = *desc;
-    d2.variant = plan->variant;
-    d2.device_cus = plan->cus;
-    spear_plan_t again;
-    st = make_plan(d2, plan->cus, &again);
-    if (st != SPEAR_OK || !same_plan(again, *plan)) return SPEAR_ERR_INVALID_PLAN;
-    p = *plan;
-  } else {
-    st = plan_for(*desc, &p);
-    if (st != SPEAR_OK) return st;
-  }
+  spear_status_t st = resolve_plan(*desc, plan, &p);
+  if (st != SPEAR_OK) return st;
   if (desc->M == 0) return SPEAR_OK;
   const bool ec = p.variant != SPEAR_VARIANT_NO_EC;
   if (!X || !Wq || !scales || !Y) return SPEAR_ERR_NULL_POINTER;
@@ -248,7 +249,13 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
 }
 
 spear_status_t spear_take_error(void* workspace, size_t workspace_bytes, void* code_out, void* stream) {
-  if (!workspace || !code_out) return SPEAR_ERR_NULL_POINTER;
+  if (!code_out) return SPEAR_ERR_NULL_POINTER;
+  if (!workspace && workspace_bytes == 0) {
+    // The allocation-free entry point's workspace on the current device.
+    if (static_scratch(&workspace, stream) != hipSuccess) return SPEAR_ERR_HIP;
+    workspace_bytes = kStaticScratchBytes;
+  }
+  if (!workspace) return SPEAR_ERR_NULL_POINTER;
   if (workspace_bytes < kSyncHeaderBytes) return SPEAR_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(workspace, 16) || !aligned(code_out, 4)) return SPEAR_ERR_MISALIGNED;
   return hip_status(launch_take_error(workspace, code_out, stream));

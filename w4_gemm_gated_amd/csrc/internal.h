@@ -81,6 +81,9 @@ EcWorkspace ec_workspace_layout(int64_t M, int64_t K, int64_t rank, int target_b
 // Host planner (pure host code; no HIP calls).
 spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* plan);
 spear_status_t check_desc(const spear_linear_desc_t& d);
+// The plan a call runs: `plan` checked against the descriptor (re-planned
+// and compared), or planned here when it is NULL.  No device work.
+spear_status_t resolve_plan(const spear_linear_desc_t& desc, const spear_plan_t* plan, spear_plan_t* out);
 
 // Shapes of the main kernel families.
 constexpr int kSkinnyMaxM = 16;   // rows handled by the skinny kernel
@@ -176,6 +179,12 @@ TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_
 // (else a second wave of tiles waits for a free CU), unless the tiles would
 // then cover less than two thirds of the GPU.
 TiledShape fused_tiled_shape(int64_t M, int64_t K, int64_t N, int cus, int ec_blocks, size_t scratch_base);
+
+// The allocation-free entry point's workspace: a file-scope device array of
+// this size (noalloc.hip), one per GPU; static_scratch returns the current
+// device's address, setting it up on first use (its header zeroed on `stream`).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** out, void* stream);
 
 // Raise a kernel's dynamic-LDS limit on the current device (once per kernel
 // and device; later calls return at once).
