@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mid", action="store_true", help="skip the mid-size-M configurations")
     ap.add_argument("--mid-steps", type=int, default=20)
+    ap.add_argument("--no-grouped", action="store_true", help="skip the group-wise (g128) variant")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--pmc-mode", action="store_true",
@@ -62,13 +63,14 @@ def log(msg):
 
 
 class Layer:
-    """R device copies of one layer's weights (same values, distinct addresses)."""
+    """R device copies of one layer's weights (same values, distinct addresses);
+    grouped: group-wise scales (one per 128 input rows) instead of per channel."""
 
-    def __init__(self, torch, sp, w, copies):
+    def __init__(self, torch, sp, w, copies, grouped=False):
         dev = "cuda:0"
         t = lambda a: None if a is None else torch.from_numpy(a).to(dev)  # noqa: E731
         W = t(w["W"])
-        Wq, s = sp.spear_pack_w4(W)
+        Wq, s = sp.spear_pack_w4_grouped(W) if grouped else sp.spear_pack_w4(W)
         del W
         A, B, wg = t(w["A"]), t(w["B"]), t(w["w_g"])
         self.sets = []
@@ -409,6 +411,11 @@ def main():
     if not args.no_mid:
         mid = mid_size(torch, sp, workloads, args.mid_steps, graph)
 
+    # ------------------------------------------------------------ group-wise scales
+    grouped = None
+    if not args.no_grouped:
+        grouped = grouped_section(torch, sp, workloads, args.steps, args.prefill_steps, graph, not args.no_prefill)
+
     # ------------------------------------------------------------ oracle on the host
     cpu = None
     if not args.no_cpu_baseline:
@@ -438,6 +445,7 @@ def main():
         "ec_overhead": overhead,
         "prefill": prefill,
         "mid_m": mid,
+        "g128": grouped,
     }
     print(json.dumps(line), flush=True)
 
@@ -521,6 +529,56 @@ def mid_size(torch, sp, workloads, steps, graph):
     out["layer_stack"] = {"tokens": 256, "weight_copies": copies, "layers": st,
                           "stack_us": round(total_on * 1e6, 2), "stack_no_ec_us": round(total_off * 1e6, 2)}
     log(f"mid-size M: layer stack {total_on * 1e6:.1f} us, EC off {total_off * 1e6:.1f} us")
+    return out
+
+
+def grouped_section(torch, sp, workloads, steps, prefill_steps, graph, do_prefill):
+    """The group-wise (g128) variant on the decode step's calls (M = 1, 4, 16 of
+    the q_proj shape) and on the prefill workload, fused, cold weights; bytes
+    count the group scales (ceil(K/128) x N_pad x 2) in place of the per-channel
+    ones."""
+    out = {}
+    w = workloads.workload(2)
+    K, N, r = w["K"], w["N"], w["r"]
+    scale_extra = -(-K // 128) * (-(-N // 16) * 16) * 2 - 2 * N
+    per_set = workloads.algorithmic_bytes(16, K, N, r) + scale_extra
+    copies = max(2, -(-COLD_BYTES // per_set))
+    lay = Layer(torch, sp, w, copies, grouped=True)
+    Ys = [torch.empty((16, N), dtype=torch.float16, device="cuda:0") for _ in range(8)]
+    dec = {}
+    for M in w["ms"]:
+        plans = {(M, v): sp.spear_dispatch_plan(M, K, N, r if v == "auto" else 0, w["b_g"][M], 0.0, v,
+                                                group_size=128) for v in ("auto", "no_ec")}
+        ws = torch.zeros(max(max(p.workspace_bytes for p in plans.values()), 1 << 20), dtype=torch.uint8,
+                         device="cuda:0")
+        t_on = time_calls(torch, [make_call(sp, lay, M, w["b_g"][M], "auto", Ys, plans, ws)], steps, 5, graph)
+        t_off = time_calls(torch, [make_call(sp, lay, M, 0.0, "no_ec", Ys, plans, ws)], steps, 5, graph)
+        b = workloads.algorithmic_bytes(M, K, N, r) + scale_extra
+        dec[str(M)] = {"us": round(t_on * 1e6, 3), "GB/s": round(b / t_on / 1e9, 1),
+                       "frac_hbm": round(b / t_on / 1e9 / HBM_PEAK_GBS, 4), "no_ec_us": round(t_off * 1e6, 3)}
+        log(f"g128 decode M={M}: {t_on * 1e6:.2f} us, EC off {t_off * 1e6:.2f} us")
+    out["decode_q_proj_4096"] = dec
+    del lay
+    if do_prefill:
+        wp = workloads.workload(3)
+        K, N, r = wp["K"], wp["N"], wp["r"]
+        pb = workloads.algorithmic_bytes(2048, K, N, r)
+        pre = Layer(torch, sp, wp, max(2, -(-COLD_BYTES // pb)), grouped=True)
+        pYs = [torch.empty((2048, N), dtype=torch.float16, device="cuda:0") for _ in range(2)]
+        plans = {(2048, v): sp.spear_dispatch_plan(2048, K, N, r if v == "auto" else 0, 0.0, 0.0, v, group_size=128)
+                 for v in ("auto", "no_ec")}
+        ws = torch.zeros(max(max(p.workspace_bytes for p in plans.values()), 1 << 20), dtype=torch.uint8,
+                         device="cuda:0")
+        t_on = min(time_calls(torch, [make_call(sp, pre, 2048, 0.0, "auto", pYs, plans, ws)], prefill_steps, 3, graph)
+                   for _ in range(2))
+        t_off = min(time_calls(torch, [make_call(sp, pre, 2048, 0.0, "no_ec", pYs, plans, ws)], prefill_steps, 3,
+                               graph) for _ in range(2))
+        main_f, _ = workloads.algorithmic_flops(2048, K, N, r)
+        out["prefill_up_proj_2048"] = {"us": round(t_on * 1e6, 2), "TFLOP/s": round(main_f / t_on / 1e12, 1),
+                                       "frac_mfma_fp16": round(main_f / t_on / 1e12 / MFMA_FP16_PEAK_TFS, 4),
+                                       "no_ec_us": round(t_off * 1e6, 2)}
+        log(f"g128 prefill: {t_on * 1e6:.1f} us, EC off {t_off * 1e6:.1f} us")
+        del pre, pYs
     return out
 
 

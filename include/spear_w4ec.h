@@ -39,9 +39,10 @@
 extern "C" {
 #endif
 
-#define SPEAR_ABI_VERSION 1u
+#define SPEAR_ABI_VERSION 2u
 #define SPEAR_LAYOUT_ID 2u
 #define SPEAR_MAX_RANK 256
+#define SPEAR_GROUP_SIZE 128   /* the one group size of group-wise scales */
 
 typedef enum spear_status {
   SPEAR_OK = 0,
@@ -73,6 +74,9 @@ typedef struct spear_linear_desc {
   float skip_tau;     /* tau in [0, 1]; 0 keeps every gate (the exact definition) */
   int32_t variant;    /* spear_variant_t */
   int32_t device_cus; /* 0: query the current device; > 0: plan for that many CUs, no device access */
+  int32_t group_size; /* 0: one scale per output channel, scales fp16 [N] (spear_pack_w4);
+                         SPEAR_GROUP_SIZE: one scale per 128 input rows and output channel,
+                         scales fp16 [ceil(K / 128), N rounded up to 16] (spear_pack_w4_grouped) */
 } spear_linear_desc_t;
 
 /* A resolved launch plan (plain data; may be cached and reused for the same
@@ -90,6 +94,7 @@ typedef struct spear_plan {
   int32_t ec_split;       /* K slices of the EC projection */
   int32_t cus;            /* compute units planned for */
   int32_t ec_local;       /* 1: every workgroup of the main launch computes the EC projection itself */
+  int32_t group_size;     /* as in the descriptor */
   size_t workspace_bytes; /* device workspace the call needs (0 = none) */
 } spear_plan_t;
 
@@ -122,6 +127,22 @@ spear_status_t spear_packed_bytes(int32_t K, int32_t N, size_t* bytes);
  */
 spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales,
                              void* stream);
+
+/*
+ * spear_pack_w4_grouped -- quantize and pack a weight with group-wise scales
+ * (SPEAR page, abstract: per-channel quantization is named the challenging
+ * setting; this is its usual counterpart, one scale per group of input rows).
+ *   W, Wq as for spear_pack_w4 (the same packed layout of the codes).
+ *   group_size  SPEAR_GROUP_SIZE (other sizes: UNSUPPORTED).
+ *   scales  output, fp16 [ceil(K / 128), N_pad] row-major, N_pad = N rounded up
+ *           to 16 (columns >= N hold 0), 16-byte aligned:
+ *           s[g, n] = fp16(max over k in [128 g, 128 g + 128) of |W[k, n]| / 7)
+ *           (the last group may be shorter); q = clamp(rint(W[k, n] / s[g, n]),
+ *           -7, 7) with g = k / 128 and the per-channel rules otherwise.
+ * Errors: NULL_POINTER, INVALID_SHAPE, UNSUPPORTED, MISALIGNED, HIP.
+ */
+spear_status_t spear_pack_w4_grouped(const void* W, int32_t K, int32_t N, int32_t group_size, void* Wq,
+                                     void* scales, void* stream);
 
 /*
  * spear_dispatch_plan -- choose the kernel-fusion variant and the launch
@@ -157,7 +178,12 @@ spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t
  *   desc     the call; plan may be NULL (planned internally) or the result of
  *            spear_dispatch_plan for the same M, K, N, rank and variant.
  *   X        fp16 [M, K], 16-byte aligned.
- *   Wq, scales  from spear_pack_w4 (16- and 2-byte aligned).
+ *   Wq, scales  from spear_pack_w4 (desc->group_size 0) or spear_pack_w4_grouped
+ *            (desc->group_size SPEAR_GROUP_SIZE) (16- and 2-byte aligned).  With group
+ *            scales the dequantized weight is q[k, n] s[k / 128, n]: the decode
+ *            kernel (M <= 16) sums each 128-k group in fp32 and scales it there,
+ *            the tile kernels scale the decoded fp16 weights (fp16(q s)) before
+ *            the matrix instructions.
  *   A        fp16 [K, rank], B fp16 [rank, N], w_g fp16 [K] (2-byte aligned;
  *            A and w_g 16-byte aligned for the fused variant); may be NULL when
  *            rank == 0 or the resolved variant is NO_EC.  Inputs must be finite.

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.spear_abi_version() == 1
+    assert lib.spear_abi_version() == 2
     for code, name in _binding.STATUS_NAMES.items():
         assert lib.spear_status_str(code).decode().startswith(name)
     assert lib.spear_status_str(99).decode() == "SPEAR_ERR_UNKNOWN"
@@ -157,7 +157,7 @@ def test_dispatch_rules(lib):
     assert st == 0 and p.variant == 3 and p.tile_m == 64 and p.split_k > 1 and p.workspace_bytes > 0
     st, p = plan(lib, 0, 512, 512, 16)
     assert st == 0
-    assert p.abi_version == 1 and p.layout_id == 2 and p.cus == 256
+    assert p.abi_version == 2 and p.layout_id == 2 and p.cus == 256
 
 
 def test_dispatch_is_deterministic(lib):
@@ -236,3 +236,23 @@ def test_ec_project_checks(lib):
     assert lib.spear_ec_project(16, 512, 16, null, fake, fake, 0.0, 0.0, fake, fake, fake, nb.value, null) == 1
     assert lib.spear_ec_project(16, 512, 16, fake, fake, fake, float("nan"), 0.0, fake, fake, fake,
                                 nb.value, null) == 8
+
+
+def test_group_scales_descriptor_and_pack_checks(lib):
+    """Group-wise scales: only groups of 128 (others UNSUPPORTED); the plan
+    carries the group size; the grouped pack checks its arguments before any
+    launch (a group size other than 128, shapes, alignment)."""
+    d = _binding.LinearDesc(16, 4096, 4096, 32, 0.0, 0.0, 0, 256, 128)
+    p = _binding.Plan()
+    assert lib.spear_dispatch_plan(ctypes.byref(d), ctypes.byref(p)) == 0
+    assert p.group_size == 128 and p.variant == 1 and p.kernel == 0
+    d = _binding.LinearDesc(2048, 4096, 14336, 64, 0.0, 0.0, 0, 256, 128)
+    assert lib.spear_dispatch_plan(ctypes.byref(d), ctypes.byref(p)) == 0
+    assert p.group_size == 128 and p.kernel == 1
+    for bad in (64, 32, 1, -1, 256):
+        d = _binding.LinearDesc(16, 4096, 4096, 32, 0.0, 0.0, 0, 256, bad)
+        assert lib.spear_dispatch_plan(ctypes.byref(d), ctypes.byref(p)) == 3
+    buf = ctypes.create_string_buffer(1024)
+    assert lib.spear_pack_w4_grouped(None, 128, 16, 128, buf, buf, None) == 1
+    assert lib.spear_pack_w4_grouped(buf, 12, 16, 128, buf, buf, None) == 2
+    assert lib.spear_pack_w4_grouped(buf, 128, 16, 64, buf, buf, None) == 3

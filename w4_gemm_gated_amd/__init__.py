@@ -19,6 +19,7 @@ from ._binding import LinearDesc, Plan, SpearError, VARIANTS, EXPORTS  # noqa: F
 __all__ = [
     "spear_packed_bytes",
     "spear_pack_w4",
+    "spear_pack_w4_grouped",
     "spear_dispatch_plan",
     "spear_w4ec_linear",
     "spear_ec_project",
@@ -47,7 +48,7 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype, dims=None):
+def _need(t, name, dtype, dims=None):  # noqa: D401 - argument check
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
@@ -81,6 +82,18 @@ def spear_pack_w4(W):
     return Wq, s
 
 
+def spear_pack_w4_grouped(W, group_size=128):
+    """W fp16 [K, N] on the GPU -> (Wq uint8 [packed bytes], scales fp16
+    [ceil(K/128), N rounded up to 16]; columns >= N hold 0)."""
+    _need(W, "W", torch.float16, 2)
+    K, N = W.shape
+    Wq = torch.empty(spear_packed_bytes(K, N), dtype=torch.uint8, device=W.device)
+    s = torch.empty((-(-K // 128), -(-N // 16) * 16), dtype=torch.float16, device=W.device)
+    st = library().spear_pack_w4_grouped(_ptr(W), K, N, int(group_size), _ptr(Wq), _ptr(s), _stream(W.device))
+    _binding.check(st, "spear_pack_w4_grouped")
+    return Wq, s
+
+
 def spear_debug_unpack_w4(Wq, K, N):
     """Packed weight -> int8 codes q [K, N] (same decode as the GEMM kernels)."""
     _need(Wq, "Wq", torch.uint8, 1)
@@ -90,14 +103,15 @@ def spear_debug_unpack_w4(Wq, K, N):
     return q
 
 
-def _desc(M, K, N, rank, gate_bias, skip_tau, variant, device_cus):
+def _desc(M, K, N, rank, gate_bias, skip_tau, variant, device_cus, group_size=0):
     v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    return LinearDesc(int(M), int(K), int(N), int(rank), float(gate_bias), float(skip_tau), v, int(device_cus))
+    return LinearDesc(int(M), int(K), int(N), int(rank), float(gate_bias), float(skip_tau), v, int(device_cus),
+                      int(group_size))
 
 
-def spear_dispatch_plan(M, K, N, rank, gate_bias=0.0, skip_tau=0.0, variant="auto", device_cus=0):
+def spear_dispatch_plan(M, K, N, rank, gate_bias=0.0, skip_tau=0.0, variant="auto", device_cus=0, group_size=0):
     """Plan a call; returns the Plan structure (see Plan.as_dict())."""
-    d = _desc(M, K, N, rank, gate_bias, skip_tau, variant, device_cus)
+    d = _desc(M, K, N, rank, gate_bias, skip_tau, variant, device_cus, group_size)
     p = Plan()
     _binding.check(library().spear_dispatch_plan(ctypes.byref(d), ctypes.byref(p)), "spear_dispatch_plan")
     return p
@@ -120,20 +134,35 @@ def _workspace(nbytes, device):
     return ws
 
 
+def _scales_shape(scales, K, N):
+    """(N, group_size) from the scale tensor: [N] per channel, or the group
+    scales [ceil(K/128), N_pad] of spear_pack_w4_grouped (N then required)."""
+    _need(scales, "scales", torch.float16)
+    if scales.dim() == 1:
+        return (scales.shape[0] if N is None else int(N)), 0
+    if N is None:
+        raise ValueError("N must be given with group scales")
+    N = int(N)
+    if scales.dim() != 2 or scales.shape != (-(-K // 128), -(-N // 16) * 16):
+        raise ValueError("group scales must be [ceil(K/128), N rounded up to 16]")
+    return N, 128
+
+
 def spear_w4ec_linear(X, Wq, scales, A, B, w_g, gate_bias, skip_tau=0.0, variant="auto",
                       N=None, plan=None, Y=None, workspace=None):
     """Y fp16 [M, N] = X . dequant(Wq, s) + g' (.) ((X . A) . B).
 
-    X fp16 [M, K]; Wq/scales from spear_pack_w4; A fp16 [K, r]; B fp16 [r, N];
-    w_g fp16 [K].  A, B, w_g may be None (rank 0).  `plan` may come from
-    spear_dispatch_plan for the same shape; `workspace` (uint8, zero-filled
-    before first use) defaults to a cached one for the current stream.
+    X fp16 [M, K]; Wq/scales from spear_pack_w4 (scales [N]) or
+    spear_pack_w4_grouped (scales [ceil(K/128), N_pad]; N required); A fp16
+    [K, r]; B fp16 [r, N]; w_g fp16 [K].  A, B, w_g may be None (rank 0).
+    `plan` may come from spear_dispatch_plan for the same shape; `workspace`
+    (uint8, zero-filled before first use) defaults to a cached one for the
+    current stream.
     """
     _need(X, "X", torch.float16, 2)
     _need(Wq, "Wq", torch.uint8, 1)
-    _need(scales, "scales", torch.float16, 1)
     M, K = X.shape
-    N = scales.shape[0] if N is None else int(N)
+    N, group = _scales_shape(scales, K, N)
     rank = 0
     if A is not None:
         _need(A, "A", torch.float16, 2)
@@ -144,7 +173,7 @@ def spear_w4ec_linear(X, Wq, scales, A, B, w_g, gate_bias, skip_tau=0.0, variant
             raise ValueError("EC shapes must be A [K, r], B [r, N], w_g [K]")
     if Wq.numel() != spear_packed_bytes(K, N):
         raise ValueError("Wq size does not match K and N")
-    d = _desc(M, K, N, rank, gate_bias, skip_tau, variant, 0)
+    d = _desc(M, K, N, rank, gate_bias, skip_tau, variant, 0, group)
     if plan is None:
         plan = Plan()
         _binding.check(library().spear_dispatch_plan(ctypes.byref(d), ctypes.byref(plan)),
@@ -170,9 +199,8 @@ def spear_w4ec_linear_noalloc(X, Wq, scales, A, B, w_g, gate_bias, skip_tau=0.0,
     not given."""
     _need(X, "X", torch.float16, 2)
     _need(Wq, "Wq", torch.uint8, 1)
-    _need(scales, "scales", torch.float16, 1)
     M, K = X.shape
-    N = scales.shape[0] if N is None else int(N)
+    N, group = _scales_shape(scales, K, N)
     rank = 0
     if A is not None:
         _need(A, "A", torch.float16, 2)
@@ -183,7 +211,7 @@ def spear_w4ec_linear_noalloc(X, Wq, scales, A, B, w_g, gate_bias, skip_tau=0.0,
             raise ValueError("EC shapes must be A [K, r], B [r, N], w_g [K]")
     if Wq.numel() != spear_packed_bytes(K, N):
         raise ValueError("Wq size does not match K and N")
-    d = _desc(M, K, N, rank, gate_bias, skip_tau, variant, 0)
+    d = _desc(M, K, N, rank, gate_bias, skip_tau, variant, 0, group)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     else:

@@ -24,6 +24,7 @@ STATUS_NAMES = {
     8: "SPEAR_ERR_INVALID_ARGUMENT",
 }
 VARIANTS = {"auto": 0, "fused": 1, "split": 2, "no_ec": 3}
+GROUP_SIZE = 128   # SPEAR_GROUP_SIZE
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 
 # Entry points declared in include/spear_w4ec.h.
@@ -32,6 +33,7 @@ EXPORTS = (
     "spear_abi_version",
     "spear_packed_bytes",
     "spear_pack_w4",
+    "spear_pack_w4_grouped",
     "spear_dispatch_plan",
     "spear_w4ec_linear",
     "spear_ec_workspace_bytes",
@@ -50,6 +52,7 @@ class LinearDesc(ctypes.Structure):
         ("M", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int32), ("rank", ctypes.c_int32),
         ("gate_bias", ctypes.c_float), ("skip_tau", ctypes.c_float),
         ("variant", ctypes.c_int32), ("device_cus", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
     ]
 
 
@@ -61,6 +64,7 @@ class Plan(ctypes.Structure):
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("split_k", ctypes.c_int32),
         ("grid", ctypes.c_int32), ("producers", ctypes.c_int32), ("ec_split", ctypes.c_int32),
         ("cus", ctypes.c_int32), ("ec_local", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -98,6 +102,8 @@ def load(path=None):
     lib.spear_packed_bytes.argtypes = [i32, i32, ctypes.POINTER(sz)]
     lib.spear_pack_w4.restype = ctypes.c_int
     lib.spear_pack_w4.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.spear_pack_w4_grouped.restype = ctypes.c_int
+    lib.spear_pack_w4_grouped.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.spear_dispatch_plan.restype = ctypes.c_int
     lib.spear_dispatch_plan.argtypes = [ctypes.POINTER(LinearDesc), ctypes.POINTER(Plan)]
     lib.spear_w4ec_linear.restype = ctypes.c_int

@@ -56,7 +56,7 @@ bool same_plan(const spear_plan_t& a, const spear_plan_t& b) {
          a.kernel == b.kernel && a.M == b.M && a.K == b.K && a.N == b.N && a.rank == b.rank &&
          a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.split_k == b.split_k &&
          a.grid == b.grid && a.producers == b.producers && a.ec_split == b.ec_split &&
-         a.cus == b.cus && a.workspace_bytes == b.workspace_bytes;
+         a.cus == b.cus && a.group_size == b.group_size && a.workspace_bytes == b.workspace_bytes;
 }
 
 spear_status_t hip_status(hipError_t e) { return e == hipSuccess ? SPEAR_OK : SPEAR_ERR_HIP; }
@@ -133,6 +133,16 @@ spear_status_t spear_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void
   return hip_status(launch_pack_w4(W, K, N, Wq, scales, stream));
 }
 
+spear_status_t spear_pack_w4_grouped(const void* W, int32_t K, int32_t N, int32_t group_size, void* Wq,
+                                     void* scales, void* stream) {
+  if (!W || !Wq || !scales) return SPEAR_ERR_NULL_POINTER;
+  if (K < 8 || K % 8 != 0 || N < 1) return SPEAR_ERR_INVALID_SHAPE;
+  if (group_size != SPEAR_GROUP_SIZE) return SPEAR_ERR_UNSUPPORTED;
+  if ((int64_t)K * 8 > INT32_MAX || (int64_t)N * 16 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
+  if (!aligned(W, 2) || !aligned(Wq, 16) || !aligned(scales, 16)) return SPEAR_ERR_MISALIGNED;
+  return hip_status(launch_pack_w4_grouped(W, K, N, Wq, scales, stream));
+}
+
 spear_status_t spear_debug_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream) {
   if (!Wq || !q_out) return SPEAR_ERR_NULL_POINTER;
   if (K < 8 || K % 8 != 0 || N < 1) return SPEAR_ERR_INVALID_SHAPE;
@@ -193,6 +203,7 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
     return SPEAR_ERR_MISALIGNED;
   if (workspace && !aligned(workspace, 16)) return SPEAR_ERR_MISALIGNED;
   if (ec && (!aligned(A, 2) || !aligned(B, 2) || !aligned(w_g, 2))) return SPEAR_ERR_MISALIGNED;
+  if (desc->group_size != 0 && !aligned(scales, 16)) return SPEAR_ERR_MISALIGNED;
   if (p.variant == SPEAR_VARIANT_FUSED && (!aligned(A, 16) || !aligned(w_g, 16))) return SPEAR_ERR_MISALIGNED;
 
   const bool skinny = p.kernel == 0;
@@ -225,6 +236,7 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
     s.workspace = workspace;
     s.Pext = ec_bytes ? (const float*)((const char*)workspace + L.p) : nullptr;
     s.gext = ec_bytes ? (const float*)((const char*)workspace + L.g) : nullptr;
+    s.grouped = desc->group_size != 0 ? 1 : 0;
     s.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     s.wait_xor = g_wait_xor.load(std::memory_order_relaxed);
     return hip_status(launch_skinny(s, stream));
@@ -243,6 +255,7 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
   }
   ga.fused = fused_tiled ? 1 : 0;
   ga.ecargs = e;
+  ga.grouped = desc->group_size != 0 ? 1 : 0;
   ga.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   ga.wait_xor = g_wait_xor.load(std::memory_order_relaxed);
   return hip_status(launch_gemm(ga, p, stream));

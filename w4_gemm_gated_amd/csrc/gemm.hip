@@ -195,7 +195,7 @@ constexpr int stages_for(int tm, bool split) { return split && tm == 64 ? 3 : 2;
 // tile.  FUSED: P and g come from EC workgroups of the same launch; the
 // epilogue waits for their ready flags (raised to `tag`) and reads P and g
 // with device-coherent loads.
-template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool FUSED>
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool FUSED, bool G>
 __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsigned char* lds, uint32_t tag) {
   static_assert(WM * WN * kWave == kGemmThreads, "four waves");
   constexpr int TM = 16 * MBW * WM;
@@ -259,6 +259,14 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     }
   };
 
+  // Group scales (G): s[kc][column] of the lane's column in each of its NBW
+  // panels (columns >= N clamped: never stored).
+  const int ncol0 = nb_base * 16 + c16;
+  auto load_s = [&](int kc, half_t* dst) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) dst[nb] = a.scales[(size_t)kc * a.NBLK * 16 + min(ncol0 + nb * 16, a.N - 1)];
+  };
+
   float4_t acc[MBW][NBW];
 #pragma unroll
   for (int i = 0; i < MBW; ++i)
@@ -267,8 +275,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
 
   const int kc_begin = split * a.CPS, kc_end = min(a.KC, kc_begin + a.CPS);
   // The matrix instructions of one 128-k step from X stage `st` and the
-  // packed words w.
-  auto compute = [&](int st, const u32x4_t* w_) {
+  // packed words w (G: each decoded fragment times its group scale, sg).
+  auto compute = [&](int st, const u32x4_t* w_, const half_t* sg) {
     const half_t* xst = xs + (size_t)st * kStageHalves;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -281,7 +289,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       }
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        const half8_t bf = decode_w4(w_[nb][j]);
+        const half8_t bf = G ? decode_w4(w_[nb][j]) * sg[nb] : decode_w4(w_[nb][j]);
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = mfma16x16x32(af[mb], bf, acc[mb][nb]);
       }
@@ -291,8 +299,10 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     // Two stages, loads one step ahead (the 256-row tiles: two X stages fill
     // the LDS).
     u32x4_t wcur[NBW], wnext[NBW];
+    half_t scur[NBW], snext[NBW];
     issue_x(kc_begin, 0);
     load_w(kc_begin, wcur);
+    if (G) load_s(kc_begin, scur);
     for (int kc = kc_begin; kc < kc_end; ++kc) {
       const int st = (kc - kc_begin) & 1;
       wait_vm_all();
@@ -300,10 +310,14 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       if (kc + 1 < kc_end) {
         issue_x(kc + 1, st ^ 1);
         load_w(kc + 1, wnext);
+        if (G) load_s(kc + 1, snext);
       }
-      compute(st, wcur);
+      compute(st, wcur, scur);
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) wcur[nb] = wnext[nb];
+      for (int nb = 0; nb < NBW; ++nb) {
+        wcur[nb] = wnext[nb];
+        if (G) scur[nb] = snext[nb];
+      }
     }
   } else {
     // Three stages, loads two steps ahead; the packed weights go through LDS
@@ -315,9 +329,22 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     // nothing reads again, so every step issues the same L copies.
     constexpr int kPanels = NBW * WN;                       // per workgroup
     constexpr int kWCopies = (kPanels + WM * WN - 1) / (WM * WN);   // per wave
-    constexpr int L = kCopiesPerWave + kWCopies;
+    // G: one 4-byte copy per lane (lanes 0..31: the wave's 64 group scales,
+    // its NBW panels, from the row of chunk kc, N padded to 16) into its own
+    // 256-byte slot per stage, ssm[stage][wave][128 halves].
+    static_assert(!G || NSTAGE != 3 || NBW * 16 == kWave, "one scale copy per wave");
+    constexpr int L = kCopiesPerWave + kWCopies + (G ? 1 : 0);
     unsigned char* wsm = lds + (size_t)NSTAGE * kStageHalves * 2;
+    half_t* ssm = reinterpret_cast<half_t*>(wsm + (size_t)NSTAGE * ((kPanels + 3) / 4 * 4) * 1024);
     const int pan0 = n_tile * kPanels;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scales, (uint32_t)((size_t)a.KC * a.NBLK * 32));
+    auto issue_s = [&](int kc, int st) {
+      if (G) {
+        const uint32_t voff = lane < kWave / 2 ? (uint32_t)nb_base * 32u + (uint32_t)lane * 4u : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void_t*)(ssm + ((size_t)st * (WM * WN) + w) * 2 * kWave), 4,
+                                                 voff, kc * a.NBLK * 32, 0, 0);
+      }
+    };
     auto issue_w = [&](int kc, int st) {
 #pragma unroll
       for (int c = 0; c < kWCopies; ++c) {
@@ -330,10 +357,12 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     const int nsteps = kc_end - kc_begin;
     issue_x(kc_begin, 0);
     issue_w(kc_begin, 0);
+    issue_s(kc_begin, 0);
     {
       const int k1 = min(kc_begin + 1, kc_end - 1);
       issue_x(k1, 1);
       issue_w(k1, 1);
+      issue_s(k1, 1);
     }
     for (int i = 0; i < nsteps; ++i) {
       const int st = i % 3;
@@ -349,11 +378,17 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       const int kn = min(kc_begin + i + 2, kc_end - 1);
       issue_x(kn, (i + 2) % 3);
       issue_w(kn, (i + 2) % 3);
+      issue_s(kn, (i + 2) % 3);
       u32x4_t wv[NBW];
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
         wv[nb] = *reinterpret_cast<const u32x4_t*>(wsm + (((size_t)st * kPanels + wn * NBW + nb) * 64 + lane) * 16);
-      compute(st, wv);
+      half_t sv[NBW];
+      if (G) {
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) sv[nb] = ssm[((size_t)st * (WM * WN) + w) * 2 * kWave + nb * 16 + c16];
+      }
+      compute(st, wv, sv);
     }
     wait_vm_all();   // the repeated copies land before the LDS is reused
   }
@@ -417,11 +452,13 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   // in the low half; rows >= rank clamped: they meet zero P columns) and
   // pg[TM][64] = fp16(g' P) of the tile's rows (rows >= M clamped: never
   // stored), after gs[TM], the tile's gates.
+  if (!G) {
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const float s = (float)a.scales[min((nb_base + nb) * 16 + c16, a.N - 1)];
+    for (int nb = 0; nb < NBW; ++nb) {
+      const float s = (float)a.scales[min((nb_base + nb) * 16 + c16, a.N - 1)];
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] *= s;
+      for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] *= s;
+    }
   }
   const int jblocks = a.ec ? a.ps / 32 : 0;
   const half_t* bs = reinterpret_cast<const half_t*>(lds);
@@ -493,7 +530,7 @@ template <int TM, int TN, int NS>
 constexpr size_t lds_bytes_for() {
   // X stages, and with three stages the packed-weight stages (TN / 16 panels
   // of 1 KiB each, one copy per wave at least).
-  constexpr size_t w_stages = NS == 3 ? (size_t)3 * ((TN / 16 + 3) / 4 * 4) * 1024 : 0;
+  constexpr size_t w_stages = NS == 3 ? (size_t)3 * ((TN / 16 + 3) / 4 * 4) * 1024 + (size_t)3 * 4 * kWave * 4 : 0;
   constexpr size_t stages = (size_t)NS * TM * kKt * 2 + w_stages;
   constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
   constexpr size_t y_tile = (size_t)TM * (TN + 8) * 2;
@@ -501,10 +538,10 @@ constexpr size_t lds_bytes_for() {
   return m > y_tile ? m : y_tile;
 }
 
-template <int MBW, int NBW, int WM, int WN, bool SPLIT>
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G>
 __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  gemm_block<MBW, NBW, WM, WN, SPLIT, false>(a, blockIdx.x, lds, 0u);
+  gemm_block<MBW, NBW, WM, WN, SPLIT, false, G>(a, blockIdx.x, lds, 0u);
 }
 
 // Fused tiled launch: blocks [0, E) are EC workgroups (the first ec_blocks
@@ -515,7 +552,7 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a
 // the EC workgroups raise.  Every block reads the call epoch first and counts
 // itself out last (count_out: the last to finish returns the finisher count
 // to zero and advances the epoch; every block has read it by then).
-template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB>
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB, bool G>
 __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs f) {
   extern __shared__ __align__(16) unsigned char lds[];
   const uint32_t tag = call_tag(f.sync);
@@ -523,47 +560,63 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs 
   if (b < f.E) {
     if (b < f.ec_blocks) ec_block<true, true, PB>(f.e, lds, b % f.e.m_tiles, b / f.e.m_tiles, tag);
   } else {
-    gemm_block<MBW, NBW, WM, WN, SPLIT, true>(f.g, b - f.E, lds, tag);
+    gemm_block<MBW, NBW, WM, WN, SPLIT, true, G>(f.g, b - f.E, lds, tag);
   }
   __syncthreads();
   if (threadIdx.x < kWave) count_out(f.sync, gridDim.x, tag);
 }
 
-template <int MBW, int NBW, int WM, int WN, bool SPLIT>
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G>
 hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
   constexpr size_t lds = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, stages_for(16 * MBW * WM, SPLIT)>();
   const hipError_t attr =
-      set_max_dynamic_lds(reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>), (int)lds);
+      set_max_dynamic_lds(reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT, G>), (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT>), dim3((unsigned)(k.MT * k.NT * k.S)),
+  hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT, G>), dim3((unsigned)(k.MT * k.NT * k.S)),
                      dim3(kGemmThreads), lds, (hipStream_t)stream, k);
   return hipGetLastError();
 }
 
-template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB>
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB, bool G>
 hipError_t launch_fused_pb(const FusedKArgs& f, void* stream) {
   const size_t tile = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, stages_for(16 * MBW * WM, SPLIT)>();
   const size_t ec = ec_lds_bytes(f.e.ss, f.e.rp);
   const size_t lds = tile > ec ? tile : ec;
   if (ec_kb_for(PB) * 32 != f.e.ss || lds > kMaxLdsBytes - 1024) return hipErrorInvalidValue;
   const hipError_t attr = set_max_dynamic_lds(
-      reinterpret_cast<const void*>(&w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB>), (int)(kMaxLdsBytes - 1024));
+      reinterpret_cast<const void*>(&w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB, G>), (int)(kMaxLdsBytes - 1024));
   if (attr != hipSuccess) return attr;
   const unsigned grid = (unsigned)(f.E + f.g.MT * f.g.NT * f.g.S);
-  hipLaunchKernelGGL((w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB>), dim3(grid), dim3(kGemmThreads), lds,
+  hipLaunchKernelGGL((w4_gemm_fused_kernel<MBW, NBW, WM, WN, SPLIT, PB, G>), dim3(grid), dim3(kGemmThreads), lds,
                      (hipStream_t)stream, f);
   return hipGetLastError();
 }
 
-template <int MBW, int NBW, int WM, int WN, bool SPLIT>
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G>
 hipError_t launch_fused(const FusedKArgs& f, void* stream) {
   switch (ec_pb_for(f.e.rank)) {
-    case 1: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 1>(f, stream);
-    case 2: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 2>(f, stream);
-    case 4: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 4>(f, stream);
-    case 8: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 8>(f, stream);
-    default: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 16>(f, stream);
+    case 1: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 1, G>(f, stream);
+    case 2: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 2, G>(f, stream);
+    case 4: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 4, G>(f, stream);
+    case 8: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 8, G>(f, stream);
+    default: return launch_fused_pb<MBW, NBW, WM, WN, SPLIT, 16, G>(f, stream);
   }
+}
+
+template <bool G>
+hipError_t launch_tiles(const GemmKArgs& k, const FusedKArgs* f, const TiledShape& t, void* stream) {
+  if (f) {
+    if (t.tm == 256 && t.tn == 224) return launch_fused<8, 7, 2, 2, false, G>(*f, stream);
+    if (t.tm == 256) return launch_fused<8, 8, 2, 2, false, G>(*f, stream);
+    if (t.tm == 128) return launch_fused<4, 4, 2, 2, true, G>(*f, stream);
+    return launch_fused<2, 4, 2, 2, true, G>(*f, stream);
+  }
+  // 256-row tiles never split; the mid-size tiles are built with the split
+  // path, which they skip when S is 1.
+  if (t.tm == 256 && t.tn == 224) return launch_cfg<8, 7, 2, 2, false, G>(k, stream);
+  if (t.tm == 256) return launch_cfg<8, 8, 2, 2, false, G>(k, stream);
+  if (t.tm == 128) return launch_cfg<4, 4, 2, 2, true, G>(k, stream);
+  return launch_cfg<2, 4, 2, 2, true, G>(k, stream);
 }
 
 }  // namespace
@@ -654,17 +707,9 @@ hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream
     k.ready = f.e.ready;
     k.ec_tiles = L.m_tiles;
     f.g = k;
-    if (t.tm == 256 && t.tn == 224) return launch_fused<8, 7, 2, 2, false>(f, stream);
-    if (t.tm == 256) return launch_fused<8, 8, 2, 2, false>(f, stream);
-    if (t.tm == 128) return launch_fused<4, 4, 2, 2, true>(f, stream);
-    return launch_fused<2, 4, 2, 2, true>(f, stream);
+    return a.grouped ? launch_tiles<true>(k, &f, t, stream) : launch_tiles<false>(k, &f, t, stream);
   }
-  // 256-row tiles never split; the mid-size tiles are built with the split
-  // path, which they skip when S is 1.
-  if (t.tm == 256 && t.tn == 224) return launch_cfg<8, 7, 2, 2, false>(k, stream);
-  if (t.tm == 256) return launch_cfg<8, 8, 2, 2, false>(k, stream);
-  if (t.tm == 128) return launch_cfg<4, 4, 2, 2, true>(k, stream);
-  return launch_cfg<2, 4, 2, 2, true>(k, stream);
+  return a.grouped ? launch_tiles<true>(k, nullptr, t, stream) : launch_tiles<false>(k, nullptr, t, stream);
 }
 
 }  // namespace spear

@@ -119,6 +119,7 @@ struct GemmArgs {
   EcArgs ecargs;       // fused: the projection's arguments (P and g in the EC workspace)
   uint32_t spin_limit; // polls before a cross-workgroup wait gives up
   uint32_t wait_xor;   // 0; nonzero (test hook) makes every wait look for a tag nobody writes
+  int32_t grouped;     // scales fp16 [KC][N], one per 128-k chunk and column (else [N])
 };
 
 // Skinny (M <= 16) kernel: tile shape, producers and workspace layout.
@@ -158,6 +159,7 @@ struct SkinnyLaunch {
   const float* gext;
   uint32_t spin_limit;      // polls before a cross-workgroup wait gives up
   uint32_t wait_xor;        // 0; nonzero (test hook) makes every wait look for a tag nobody writes
+  int32_t grouped;          // scales fp16 [KC][N], one per 128-k chunk and column (else [N])
 };
 hipError_t launch_skinny(const SkinnyLaunch& L, void* stream);
 
@@ -192,6 +194,7 @@ hipError_t set_max_dynamic_lds(const void* kernel, int bytes);
 hipError_t launch_take_error(void* workspace, void* out, void* stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, int grid, void* sink, void* stream);
 hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
+hipError_t launch_pack_w4_grouped(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);
 hipError_t launch_ec_project(const EcArgs& a, void* stream);
 hipError_t launch_gemm(const GemmArgs& a, const spear_plan_t& plan, void* stream);

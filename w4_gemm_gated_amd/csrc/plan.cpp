@@ -30,6 +30,7 @@ spear_status_t check_desc(const spear_linear_desc_t& d) {
   if (!std::isfinite(d.gate_bias) || !std::isfinite(d.skip_tau)) return SPEAR_ERR_INVALID_ARGUMENT;
   if (d.skip_tau < 0.0f || d.skip_tau > 1.0f) return SPEAR_ERR_INVALID_ARGUMENT;
   if (d.device_cus < 0) return SPEAR_ERR_INVALID_ARGUMENT;
+  if (d.group_size != 0 && d.group_size != SPEAR_GROUP_SIZE) return SPEAR_ERR_UNSUPPORTED;
   // Index arithmetic inside the kernels uses 32-bit row and column counts.
   if ((int64_t)d.K * 8 > INT32_MAX || (int64_t)d.N * 16 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
   return SPEAR_OK;
@@ -44,6 +45,7 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
   p.layout_id = SPEAR_LAYOUT_ID;
   p.M = d.M; p.K = d.K; p.N = d.N; p.rank = d.rank;
   p.cus = cus;
+  p.group_size = d.group_size;
   const bool skinny = d.M <= kSkinnyMaxM;
   const bool ec = d.rank > 0 && d.variant != SPEAR_VARIANT_NO_EC;
   // The fused EC workgroups copy A rows verbatim (16-byte units) and read it
@@ -111,6 +113,8 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     // X and the packed weight are addressed with 32-bit buffer offsets.
     if ((int64_t)d.M * d.K * 2 > INT32_MAX || n_pad(d.N) * k_pad(d.K) / 2 > INT32_MAX)
       return SPEAR_ERR_UNSUPPORTED;
+    // Group scales are addressed the same way (2 bytes per 128 k and column).
+    if (d.group_size != 0 && n_pad(d.N) * (k_pad(d.K) / 128) * 2 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
     const TiledShape t = p.variant == SPEAR_VARIANT_FUSED ? fused_tiled_shape(d.M, d.K, d.N, cus, ec_blocks, scratch_base)
                                                           : tiled_shape(d.M, d.K, d.N, cus, scratch_base);
     if (!t.fits) return SPEAR_ERR_UNSUPPORTED;

@@ -547,8 +547,10 @@ __device__ void gather_handoff(const SkinnyKArgs& a, __amdgpu_buffer_rsrc_t hr, 
 
 // EXACT: every wave owns exactly CPW chunks (no validity test, so no load
 // ends up under a branch).  ECM: the EC mode (0 none, 1 fused, 2 split), fixed
-// at compile time so the loads of each mode are straight-line code.
-template <int NBW, int CPW, bool EXACT, int ECM>
+// at compile time so the loads of each mode are straight-line code.  G: group
+// scales (one per 128-k chunk and column): each chunk's products are summed
+// apart and scaled into the accumulator in fp32; the epilogue applies none.
+template <int NBW, int CPW, bool EXACT, int ECM, bool G>
 __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kThreads) skinny_kernel(SkinnyKArgs a) {
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   __shared__ float4_t red[3][kWave][NBW];
@@ -621,10 +623,22 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
     for (uint32_t i = 0; i < a.stream_delay; ++i) __builtin_amdgcn_s_sleep(1);
   }
 
-  // Scales of this lane's columns (columns >= N are clamped, never stored).
+  // Scales of this lane's columns (columns >= N are clamped, never stored);
+  // group scales: those of each of the wave's chunks.
   half_t scr[NBW];
+  half_t sg[G ? CPW : 1][NBW];
+  if (!G) {
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) scr[nb] = a.scales[min(n0 + nb * 16 + c16, a.N - 1)];
+    for (int nb = 0; nb < NBW; ++nb) scr[nb] = a.scales[min(n0 + nb * 16 + c16, a.N - 1)];
+  } else {
+#pragma unroll
+    for (int c = 0; c < (G ? CPW : 1); ++c) {
+      const int kc = min(wbeg + c, a.KC - 1);   // chunks past the range meet zero X
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+        sg[c][nb] = a.scales[(size_t)kc * a.NBLK * 16 + min(n0 + nb * 16 + c16, a.N - 1)];
+    }
+  }
 
   // ---- issue every load of this wave's K range.  Chunk validity is uniform
   // over the wave.
@@ -660,12 +674,27 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
   float4_t acc[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) acc[nb] = zero_float4();
+  if (!G) {
 #pragma unroll
-  for (int c = 0; c < CPW; ++c)
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) acc[nb] = mfma16x16x32(xa[c][j], decode_w4(bw[c][nb][j]), acc[nb]);
+        for (int nb = 0; nb < NBW; ++nb) acc[nb] = mfma16x16x32(xa[c][j], decode_w4(bw[c][nb][j]), acc[nb]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      float4_t part[NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) part[nb] = zero_float4();
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) part[nb] = mfma16x16x32(xa[c][j], decode_w4(bw[c][nb][j]), part[nb]);
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) acc[nb] += part[nb] * (float)sg[G ? c : 0][nb];
+    }
+  }
 
   // ---- EC operands -> LDS (then what the registers did not cover)
   if (ECM) {
@@ -813,7 +842,7 @@ __global__ void __launch_bounds__(ECM == 3 ? kThreads + kLocalWaves * kWave : kT
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     const int col = n0 + nb * 16 + c16;
-    const float sc = (float)scr[nb];
+    const float sc = G ? 1.0f : (float)scr[nb];
     if (col < a.N) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -831,45 +860,52 @@ hipError_t allow_full_lds() {
   return set_max_dynamic_lds(reinterpret_cast<const void*>(Kernel), (int)(kMaxLdsBytes - static_lds_bytes(NBW)));
 }
 
-template <int NBW, int CPW, bool EXACT>
+template <int NBW, int CPW, bool EXACT, bool G>
 hipError_t launch_exact(const SkinnyKArgs& k, size_t lds, void* stream) {
   const dim3 grid(k.P + k.T * k.S), block(kThreads);
   hipError_t e = hipSuccess;
   if (k.ec_mode == 3) {
-    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 3>, NBW>();
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 3, G>, NBW>();
     if (e == hipSuccess)
-      hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 3>), grid, dim3(kThreads + kLocalWaves * kWave), lds,
+      hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 3, G>), grid, dim3(kThreads + kLocalWaves * kWave), lds,
                          (hipStream_t)stream, k);
   } else if (k.ec_mode == 1) {
-    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 1>, NBW>();
-    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 1>), grid, block, lds, (hipStream_t)stream, k);
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 1, G>, NBW>();
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 1, G>), grid, block, lds, (hipStream_t)stream, k);
   } else if (k.ec_mode == 2) {
-    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 2>, NBW>();
-    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 2>), grid, block, lds, (hipStream_t)stream, k);
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 2, G>, NBW>();
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 2, G>), grid, block, lds, (hipStream_t)stream, k);
   } else {
-    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 0>, NBW>();
-    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 0>), grid, block, lds, (hipStream_t)stream, k);
+    e = allow_full_lds<&skinny_kernel<NBW, CPW, EXACT, 0, G>, NBW>();
+    if (e == hipSuccess) hipLaunchKernelGGL((skinny_kernel<NBW, CPW, EXACT, 0, G>), grid, block, lds, (hipStream_t)stream, k);
   }
   return e != hipSuccess ? e : hipGetLastError();
 }
 
-template <int NBW, int CPW>
+template <int NBW, int CPW, bool G>
 hipError_t launch_nbw_cpw(const SkinnyKArgs& k, bool exact, size_t lds, void* stream) {
-  return exact ? launch_exact<NBW, CPW, true>(k, lds, stream) : launch_exact<NBW, CPW, false>(k, lds, stream);
+  return exact ? launch_exact<NBW, CPW, true, G>(k, lds, stream) : launch_exact<NBW, CPW, false, G>(k, lds, stream);
 }
 
 constexpr int kMaxCpw = 8;   // chunks per wave kept in flight (NBW <= 2)
 
-template <int NBW>
+template <int NBW, bool G>
 hipError_t launch_nbw(const SkinnyKArgs& k, int cpw, bool exact, size_t lds, void* stream) {
-  if (cpw <= 1) return launch_nbw_cpw<NBW, 1>(k, exact, lds, stream);
-  if (cpw <= 2) return launch_nbw_cpw<NBW, 2>(k, exact, lds, stream);
+  if (cpw <= 1) return launch_nbw_cpw<NBW, 1, G>(k, exact, lds, stream);
+  if (cpw <= 2) return launch_nbw_cpw<NBW, 2, G>(k, exact, lds, stream);
   if constexpr (NBW == 4) {
-    return launch_nbw_cpw<NBW, 4>(k, exact, lds, stream);
+    return launch_nbw_cpw<NBW, 4, G>(k, exact, lds, stream);
   } else {
-    if (cpw <= 4) return launch_nbw_cpw<NBW, 4>(k, exact, lds, stream);
-    return launch_nbw_cpw<NBW, 8>(k, exact, lds, stream);
+    if (cpw <= 4) return launch_nbw_cpw<NBW, 4, G>(k, exact, lds, stream);
+    return launch_nbw_cpw<NBW, 8, G>(k, exact, lds, stream);
   }
+}
+
+template <bool G>
+hipError_t launch_g(const SkinnyKArgs& k, int nbw, int cpw, bool exact, size_t lds, void* stream) {
+  if (nbw == 4) return launch_nbw<4, G>(k, cpw, exact, lds, stream);
+  if (nbw == 2) return launch_nbw<2, G>(k, cpw, exact, lds, stream);
+  return launch_nbw<1, G>(k, cpw, exact, lds, stream);
 }
 
 }  // namespace
@@ -994,9 +1030,8 @@ hipError_t launch_skinny(const SkinnyLaunch& L, void* stream) {
   size_t lds = k.P > 0 ? sh.lds : 0;
   if (L.ec_mode && sh.lds_gemm > lds) lds = sh.lds_gemm;
   const bool exact = sh.CPS == 4 * sh.CPW && (int64_t)sh.CPS * sh.S == k.KC;
-  if (sh.nbw == 4) return launch_nbw<4>(k, sh.CPW, exact, lds, stream);
-  if (sh.nbw == 2) return launch_nbw<2>(k, sh.CPW, exact, lds, stream);
-  return launch_nbw<1>(k, sh.CPW, exact, lds, stream);
+  if (L.grouped) return launch_g<true>(k, sh.nbw, sh.CPW, exact, lds, stream);
+  return launch_g<false>(k, sh.nbw, sh.CPW, exact, lds, stream);
 }
 
 }  // namespace spear
