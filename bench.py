@@ -411,6 +411,11 @@ def main():
     if not args.no_mid:
         mid = mid_size(torch, sp, workloads, args.mid_steps, graph)
 
+    # ------------------------------------------------------------ EC scheduler
+    scheduler = None
+    if not args.no_mid:
+        scheduler = ec_scheduler_section(torch, sp, workloads, args.mid_steps, graph)
+
     # ------------------------------------------------------------ group-wise scales
     grouped = None
     if not args.no_grouped:
@@ -446,6 +451,8 @@ def main():
         "prefill": prefill,
         "mid_m": mid,
         "g128": grouped,
+        "ec_scheduler": scheduler,
+        "cost_model": cost_model_report(sp, per_m, prefill, mid),
     }
     print(json.dumps(line), flush=True)
 
@@ -579,6 +586,94 @@ def grouped_section(torch, sp, workloads, steps, prefill_steps, graph, do_prefil
                                        "no_ec_us": round(t_off * 1e6, 2)}
         log(f"g128 prefill: {t_on * 1e6:.1f} us, EC off {t_off * 1e6:.1f} us")
         del pre, pYs
+    return out
+
+
+def cost_model_report(sp, per_m, prefill, mid):
+    """The planner's predicted time (predicted_us, predicted_no_ec_us) beside
+    each measured call of this run: the decode step's calls, prefill, and the
+    mixed-gate and layer-stack calls."""
+    rows = []
+
+    def add(name, M, K, N, r, b_g, meas_on, meas_off):
+        p = sp.spear_dispatch_plan(M, K, N, r, b_g)
+        rows.append({"call": name, "predicted_us": round(float(p.predicted_us), 2), "measured_us": meas_on,
+                     "predicted_no_ec_us": round(float(p.predicted_no_ec_us), 2), "measured_no_ec_us": meas_off})
+    for M, d in per_m.items():
+        add(f"decode q_proj M={M}", int(M), 4096, 4096, 32, -1.0, d["us"], d["no_ec_us"])
+    if prefill:
+        add("prefill up_proj M=2048", 2048, 4096, 14336, 64, 0.0, prefill["us"], prefill["no_ec_us"])
+    if mid:
+        for M, d in mid["mixed_gate_down_proj"]["per_m"].items():
+            add(f"mixed-gate down_proj M={M}", int(M), 14336, 4096, 64, -5.9, d["fused_us"], d["no_ec_us"])
+        for name, d in mid["layer_stack"]["layers"].items():
+            if d["ec"]:
+                add(f"stack {name} M=256", 256, d["K"], d["N"], 32, 0.0, d["us"], d["no_ec_us"])
+    errs = [abs(r["predicted_us"] / r["measured_us"] - 1) for r in rows if r["measured_us"]]
+    errs += [abs(r["predicted_no_ec_us"] / r["measured_no_ec_us"] - 1) for r in rows if r["measured_no_ec_us"]]
+    errs.sort()
+    return {"rows": rows, "median_abs_rel_error": round(errs[len(errs) // 2], 4) if errs else None,
+            "max_abs_rel_error": round(errs[-1], 4) if errs else None}
+
+
+def ec_scheduler_section(torch, sp, workloads, steps, graph):
+    """The SLO-constrained EC scheduler (spear_schedule_ec) on the small-model
+    layer stack (7 linears, ECs on q, o, up, down, equal weights): a trace of
+    the 8 requests of the stack workload (a prefill of their 256 prompt tokens,
+    then decode steps of one token per unfinished request, each request
+    generating as many tokens as its prompt holds, a reading) under per-step
+    SLOs halfway between the stack's predicted time with every EC off and every
+    EC on (at M = 256 for the prefill step, M = 8 for decode steps); reported:
+    the steps whose predicted time fits, the share of EC layer-steps kept on,
+    and for the prefill step and an M = 8 decode step the measured time of the
+    chosen configuration beside the model's prediction."""
+    dev = "cuda:0"
+    layers = [workloads.stack_layer(i) for i in range(7)]
+    sched = [(L["K"], L["N"], L["r"], 0, 1.0 if L["r"] else 0.0) for L in layers]
+    prompts = list(workloads.STACK_REQUESTS)
+    gen = list(prompts)                                   # tokens each request generates
+
+    def bounds(M):
+        on, t_on = sp.spear_schedule_ec(sched, M, 1e12)
+        off = sum(float(sp.spear_dispatch_plan(M, L["K"], L["N"], L["r"], 0.0).predicted_no_ec_us) for L in layers)
+        return off, t_on
+
+    off_p, on_p = bounds(sum(prompts))
+    off_d, on_d = bounds(len(prompts))
+    slo_p, slo_d = off_p + 0.5 * (on_p - off_p), off_d + 0.5 * (on_d - off_d)
+    trace = [sum(prompts)] + [sum(1 for g in gen if g > t) for t in range(max(gen))]
+    fit, kept, ec_steps, choices = 0, 0, 0, {}
+    for i, M in enumerate(trace):
+        slo = slo_p if i == 0 else slo_d
+        on, t = sp.spear_schedule_ec(sched, M, slo)
+        fit += t <= slo + 1e-9
+        kept += sum(on)
+        ec_steps += sum(1 for L in layers if L["r"])
+        choices.setdefault(M, (on, t))
+    out = {"slo_us": {"prefill_M256": round(slo_p, 2), "decode_M8": round(slo_d, 2)},
+           "predicted_all_off_us": {"prefill_M256": round(off_p, 2), "decode_M8": round(off_d, 2)},
+           "predicted_all_on_us": {"prefill_M256": round(on_p, 2), "decode_M8": round(on_d, 2)},
+           "steps": len(trace), "steps_within_slo": int(fit), "ec_kept_share": round(kept / ec_steps, 4)}
+    # measured: the chosen configurations of the prefill step and an M = 8 step
+    meas = {}
+    per_set = sum(workloads.algorithmic_bytes(256, L["K"], L["N"], L["r"]) for L in layers)
+    copies = max(2, -(-COLD_BYTES // per_set))
+    lays = [Layer(torch, sp, L, copies) for L in layers]
+    ws = torch.zeros(32 << 20, dtype=torch.uint8, device=dev)
+    for name, M in (("prefill_M256", trace[0]), ("decode_M8", len(prompts))):
+        on, t_pred = choices[M]
+        calls = []
+        for L, lay, keep in zip(layers, lays, on):
+            v = "auto" if keep else "no_ec"
+            plan = sp.spear_dispatch_plan(M, L["K"], L["N"], L["r"] if keep else 0, 0.0, 0.0, v)
+            Ys = [torch.empty((M, L["N"]), dtype=torch.float16, device=dev) for _ in range(2)]
+            calls.append(make_call(sp, lay, M, 0.0, v, Ys, {(M, v): plan}, ws))
+        t = time_calls(torch, calls, steps, 5, graph)
+        meas[name] = {"ec_on": [L["name"] for L, k in zip(layers, on) if k], "predicted_us": round(t_pred, 2),
+                      "measured_us": round(t * 1e6, 2)}
+        log(f"scheduler {name}: ECs kept {meas[name]['ec_on']}, predicted {t_pred:.1f} us, measured {t * 1e6:.1f} us")
+    out["chosen"] = meas
+    del lays
     return out
 
 

@@ -95,8 +95,18 @@ typedef struct spear_plan {
   int32_t cus;            /* compute units planned for */
   int32_t ec_local;       /* 1: every workgroup of the main launch computes the EC projection itself */
   int32_t group_size;     /* as in the descriptor */
+  float predicted_us;       /* cost model: predicted time of this call (microseconds, MI355X) */
+  float predicted_no_ec_us; /* cost model: the same call with the EC switched off */
   size_t workspace_bytes; /* device workspace the call needs (0 = none) */
 } spear_plan_t;
+
+/* One linear layer of a batch, as the EC scheduler sees it. */
+typedef struct spear_sched_layer {
+  int32_t K, N, rank;   /* rank 0: the layer has no EC */
+  int32_t group_size;   /* 0 or SPEAR_GROUP_SIZE, as in spear_linear_desc_t */
+  float weight;         /* value of keeping this layer's EC on (>= 0), e.g. its share of the
+                           error the ECs remove; layers of equal weight are equally worth it */
+} spear_sched_layer_t;
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* spear_status_str(spear_status_t status);
@@ -165,10 +175,52 @@ spear_status_t spear_pack_w4_grouped(const void* W, int32_t K, int32_t N, int32_
  * 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value
  * decision (skip the EC term of a tile whose gates are all below tau) is
  * taken on the device inside the epilogue, so no gate value ever crosses to
- * the host.
+ * the host.  The plan also carries the cost model's predicted time of the
+ * call and of the same call with the EC off (a roofline with constants fitted
+ * to this library's measured kernels on MI355X: launch, HBM stream, matrix
+ * rate of the tile family, split-K exchange, and the variant's EC cost).
  * Errors: NULL_POINTER, INVALID_SHAPE, INVALID_ARGUMENT, UNSUPPORTED, HIP.
  */
 spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t* plan);
+
+/*
+ * spear_schedule_ec -- the SLO-constrained, EC-aware choice for one batch
+ * (SPEAR page, abstract: a scheduler that decides under a latency objective
+ * where the error compensators run).  For M tokens through the n_layers
+ * linears, choose which layers keep their EC so that the predicted latency of
+ * the batch (the sum over layers of spear_dispatch_plan's predicted_us with
+ * the EC on, predicted_no_ec_us with it off) stays within slo_us, and the
+ * total weight of the ECs kept on is the largest possible.  Exact 0/1
+ * knapsack over the layers' extra time (EC on minus off), each rounded up to
+ * a grid of at most 65536 steps of the slack (so rounding never breaks the
+ * objective); among optimal sets the one that adds the least time.
+ *   layers   host array [n_layers]; ec_on  host output [n_layers] (1: keep the
+ *            EC; always 0 for rank 0); predicted_us host output (may be NULL):
+ *            the batch's predicted latency under the choice.
+ *   device_cus  as in spear_linear_desc_t (0: query the current device).
+ * When even every EC off exceeds slo_us, all are off and predicted_us says by
+ * how much (status SPEAR_OK).  Host only; nothing is enqueued.
+ * Errors: NULL_POINTER, INVALID_SHAPE (a layer, M < 1, n_layers < 0),
+ *         INVALID_ARGUMENT (slo_us or a weight not finite, weight < 0),
+ *         UNSUPPORTED, HIP.
+ */
+spear_status_t spear_schedule_ec(const spear_sched_layer_t* layers, int32_t n_layers, int32_t M, double slo_us,
+                                 int32_t device_cus, uint8_t* ec_on, double* predicted_us);
+
+/*
+ * spear_schedule_ec_costs -- the selection step of spear_schedule_ec on costs
+ * the caller gives: among the layers i with extra_us[i] >= 0 (a negative extra
+ * marks a layer without an EC) and weight[i] > 0, the set of largest total
+ * weight whose extra times, each rounded up to the grid unit
+ * u = max(slack_us / 65536, 1e-9), sum to at most floor(slack_us / u) units;
+ * ties go to the set of fewer units.  Weights are summed in layer order.
+ * slack_us < 0: nothing is chosen.  ec_on host output [n]; added_us (may be
+ * NULL): the chosen extra time.  Host only.
+ * Errors: NULL_POINTER, INVALID_SHAPE (n outside [0, 4096]),
+ *         INVALID_ARGUMENT (a value not finite, a weight < 0).
+ */
+spear_status_t spear_schedule_ec_costs(const double* extra_us, const float* weight, int32_t n, double slack_us,
+                                       uint8_t* ec_on, double* added_us);
 
 /*
  * spear_w4ec_linear -- Y = X . dequant(Wq, s) + g' (.) ((X . A) . B).

@@ -36,6 +36,11 @@ Pins (tests marked ``not gpu``):
     dense correction X (q s + A B); brute-force scalar loops on tiny shapes;
     exactly rounded sums (math.fsum) at sampled outputs; linearity in g.
 
+The scheduler's selection step (``oracle.spear_sched``, a submodule): every
+subset of the candidate layers enumerated under the documented grid rule;
+pinned by hand-worked instances, special cases, monotonicity in the slack and
+scipy's MILP solver on the same integer knapsack.
+
 Parity unpinned: none of the functions here.  The quality claim of the
 abstract (perplexity-gap recovery) is outside this oracle.
 """

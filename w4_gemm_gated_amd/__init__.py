@@ -21,6 +21,8 @@ __all__ = [
     "spear_pack_w4",
     "spear_pack_w4_grouped",
     "spear_dispatch_plan",
+    "spear_schedule_ec",
+    "spear_schedule_ec_costs",
     "spear_w4ec_linear",
     "spear_ec_project",
     "spear_debug_unpack_w4",
@@ -115,6 +117,32 @@ def spear_dispatch_plan(M, K, N, rank, gate_bias=0.0, skip_tau=0.0, variant="aut
     p = Plan()
     _binding.check(library().spear_dispatch_plan(ctypes.byref(d), ctypes.byref(p)), "spear_dispatch_plan")
     return p
+
+
+def spear_schedule_ec(layers, M, slo_us, device_cus=0):
+    """layers: sequence of (K, N, rank, group_size, weight).  Returns (ec_on
+    list of bools, predicted batch latency in us) for a batch of M tokens."""
+    n = len(layers)
+    arr = (_binding.SchedLayer * max(n, 1))()
+    for i, (K, N, r, g, wt) in enumerate(layers):
+        arr[i] = _binding.SchedLayer(int(K), int(N), int(r), int(g), float(wt))
+    on = (ctypes.c_uint8 * max(n, 1))()
+    pred = ctypes.c_double(0.0)
+    st = library().spear_schedule_ec(arr, n, int(M), float(slo_us), int(device_cus), on, ctypes.byref(pred))
+    _binding.check(st, "spear_schedule_ec")
+    return [bool(on[i]) for i in range(n)], float(pred.value)
+
+
+def spear_schedule_ec_costs(extra_us, weights, slack_us):
+    """The scheduler's selection step on given costs: (ec_on list, added us)."""
+    n = len(extra_us)
+    ex = (ctypes.c_double * max(n, 1))(*[float(x) for x in extra_us])
+    wt = (ctypes.c_float * max(n, 1))(*[float(x) for x in weights])
+    on = (ctypes.c_uint8 * max(n, 1))()
+    added = ctypes.c_double(0.0)
+    st = library().spear_schedule_ec_costs(ex, wt, n, float(slack_us), on, ctypes.byref(added))
+    _binding.check(st, "spear_schedule_ec_costs")
+    return [bool(on[i]) for i in range(n)], float(added.value)
 
 
 # Zero-filled workspaces, one per (device, stream); every call leaves its

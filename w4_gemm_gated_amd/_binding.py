@@ -35,6 +35,8 @@ EXPORTS = (
     "spear_pack_w4",
     "spear_pack_w4_grouped",
     "spear_dispatch_plan",
+    "spear_schedule_ec",
+    "spear_schedule_ec_costs",
     "spear_w4ec_linear",
     "spear_ec_workspace_bytes",
     "spear_ec_project",
@@ -65,6 +67,7 @@ class Plan(ctypes.Structure):
         ("grid", ctypes.c_int32), ("producers", ctypes.c_int32), ("ec_split", ctypes.c_int32),
         ("cus", ctypes.c_int32), ("ec_local", ctypes.c_int32),
         ("group_size", ctypes.c_int32),
+        ("predicted_us", ctypes.c_float), ("predicted_no_ec_us", ctypes.c_float),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -72,6 +75,11 @@ class Plan(ctypes.Structure):
         d = {name: getattr(self, name) for name, _ in self._fields_}
         d["variant_name"] = VARIANT_NAMES.get(self.variant, "?")
         return d
+
+
+class SchedLayer(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("weight", ctypes.c_float)]
 
 
 class SpearError(RuntimeError):
@@ -106,6 +114,13 @@ def load(path=None):
     lib.spear_pack_w4_grouped.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.spear_dispatch_plan.restype = ctypes.c_int
     lib.spear_dispatch_plan.argtypes = [ctypes.POINTER(LinearDesc), ctypes.POINTER(Plan)]
+    lib.spear_schedule_ec.restype = ctypes.c_int
+    lib.spear_schedule_ec.argtypes = [ctypes.POINTER(SchedLayer), i32, i32, ctypes.c_double, i32,
+                                      ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_double)]
+    lib.spear_schedule_ec_costs.restype = ctypes.c_int
+    lib.spear_schedule_ec_costs.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_float), i32,
+                                            ctypes.c_double, ctypes.POINTER(ctypes.c_uint8),
+                                            ctypes.POINTER(ctypes.c_double)]
     lib.spear_w4ec_linear.restype = ctypes.c_int
     lib.spear_w4ec_linear.argtypes = [ctypes.POINTER(LinearDesc), ctypes.POINTER(Plan),
                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]

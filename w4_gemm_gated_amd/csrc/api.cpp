@@ -56,7 +56,8 @@ bool same_plan(const spear_plan_t& a, const spear_plan_t& b) {
          a.kernel == b.kernel && a.M == b.M && a.K == b.K && a.N == b.N && a.rank == b.rank &&
          a.tile_m == b.tile_m && a.tile_n == b.tile_n && a.split_k == b.split_k &&
          a.grid == b.grid && a.producers == b.producers && a.ec_split == b.ec_split &&
-         a.cus == b.cus && a.group_size == b.group_size && a.workspace_bytes == b.workspace_bytes;
+         a.cus == b.cus && a.group_size == b.group_size && a.workspace_bytes == b.workspace_bytes &&
+         a.predicted_us == b.predicted_us && a.predicted_no_ec_us == b.predicted_no_ec_us;
 }
 
 spear_status_t hip_status(hipError_t e) { return e == hipSuccess ? SPEAR_OK : SPEAR_ERR_HIP; }

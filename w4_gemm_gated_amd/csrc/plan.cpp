@@ -16,6 +16,7 @@
 //     a wave's rows is below tau) is taken on the device in the epilogue.
 //   * main kernel family by M: skinny (M <= 16 rows) or tiled (256-row tiles;
 //     128- or 64-row tiles with K split where those would not fill the GPU).
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -35,6 +36,69 @@ spear_status_t check_desc(const spear_linear_desc_t& d) {
   if ((int64_t)d.K * 8 > INT32_MAX || (int64_t)d.N * 16 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
   return SPEAR_OK;
 }
+
+// ------------------------------------------------------------ cost model
+// Predicted time of a call (microseconds) from its plan: a roofline with
+// constants fitted to this library's kernels measured on MI355X (graph replay,
+// cold weights):
+//   t = launch + max(bytes / stream rate, main flops / matrix rate of the
+//       kernel family) + split-K exchange + the variant's EC cost.
+// Stream rate: a plain read of B bytes in one launch takes 1.65 us + B / 7.2
+// TB/s (8 MiB .. 256 MiB); the decode kernel streams at 4.64 TB/s after 2.6 us
+// (its EC-off calls of 8.4 and 29.4 MB).  Matrix rates: the 256-row tiles
+// reach 1.13 PF/s on the prefill shape, the 128- and 64-row tiles 0.87 and
+// 0.55 (mid-size M, K split), the decode kernel 0.26 (its M = 16 call over
+// M = 1).  EC cost: decode hand-off 3 us, 0.07 per producer and 0.08 per KiB
+// of a producer's A slab past 32 KiB; local EC 1.0 us plus every workgroup's
+// read of A from L2,
+// fused tiles 4 us plus the EC workgroups' read of X (1.3 TB/s, partly under
+// the GEMM), split variant one more launch plus its read of X and its flops.
+namespace {
+
+struct CostConstants {
+  double stream_bytes_per_us = 7.2e6, skinny_stream_bytes_per_us = 4.64e6;
+  double launch_skinny_us = 2.6, launch_tiled_us = 3.0;
+  double mma_skinny = 0.26e9, mma_64 = 0.55e9, mma_128 = 0.87e9, mma_256 = 1.13e9;   // flop per us
+  double split_skinny_us = 2.0, split_tiled_us = 3.0;
+  double ec_handoff_us = 3.0, ec_handoff_per_producer_us = 0.07, ec_handoff_per_slab_kib_us = 0.08;
+  double ec_local_us = 1.0, l2_bytes_per_us = 30e6;
+  double ec_fused_tiled_us = 4.0, ec_fused_x_bytes_per_us = 1.3e6;
+  double ec_split_launch_us = 3.0, ec_split_x_bytes_per_us = 2.0e6, ec_split_flops_per_us = 0.5e9;
+};
+
+double predict_call_us(const spear_plan_t& p) {
+  const CostConstants c;
+  const double M = p.M, K = p.K, N = p.N, r = p.rank;
+  const bool ec = p.variant != SPEAR_VARIANT_NO_EC && p.rank > 0;
+  const bool skinny = p.kernel == 0;
+  const double scale_bytes = p.group_size ? (double)(k_pad(p.K) / 128) * (double)n_pad(p.N) * 2.0 : 2.0 * N;
+  double bytes = K * N / 2.0 + scale_bytes + 2.0 * M * K + 2.0 * M * N;
+  if (ec) bytes += 2.0 * r * (K + N) + 2.0 * K;
+  const double mma_rate = skinny ? c.mma_skinny : p.tile_m >= 256 ? c.mma_256 : p.tile_m >= 128 ? c.mma_128 : c.mma_64;
+  double t = (skinny ? c.launch_skinny_us : c.launch_tiled_us) +
+             std::max(bytes / (skinny ? c.skinny_stream_bytes_per_us : c.stream_bytes_per_us),
+                      2.0 * M * K * N / mma_rate);
+  if (p.split_k > 1) t += skinny ? c.split_skinny_us : c.split_tiled_us;
+  if (ec) {
+    const double ec_flops = 2.0 * M * (K * (r + 1) + r * N);
+    if (p.variant == SPEAR_VARIANT_SPLIT) {
+      t += c.ec_split_launch_us + 2.0 * M * K / c.ec_split_x_bytes_per_us + ec_flops / c.ec_split_flops_per_us;
+    } else if (skinny && p.ec_local) {
+      t += c.ec_local_us + 2.0 * K * r * (double)p.grid / c.l2_bytes_per_us;
+    } else if (skinny) {
+      // The producers' chain: their count (the hand-off each consumer reads)
+      // and their A slab beyond 32 KiB (the slab each one streams).
+      const double slab_kib = std::ceil(K / std::max(1, p.producers)) * r * 2.0 / 1024.0;
+      t += c.ec_handoff_us + c.ec_handoff_per_producer_us * p.producers +
+           c.ec_handoff_per_slab_kib_us * std::max(0.0, slab_kib - 32.0);
+    } else {
+      t += c.ec_fused_tiled_us + 2.0 * M * K / c.ec_fused_x_bytes_per_us;
+    }
+  }
+  return t;
+}
+
+}  // namespace
 
 spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* plan) {
   const spear_status_t st = check_desc(d);
@@ -126,6 +190,15 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     if (t.ws_bytes > ws) ws = t.ws_bytes;
   }
   p.workspace_bytes = d.M > 0 ? ws : 0;
+  p.predicted_us = (float)predict_call_us(p);
+  p.predicted_no_ec_us = p.predicted_us;
+  if (p.variant != SPEAR_VARIANT_NO_EC) {
+    spear_linear_desc_t off = d;
+    off.rank = 0;
+    off.variant = SPEAR_VARIANT_NO_EC;
+    spear_plan_t po;
+    if (make_plan(off, cus, &po) == SPEAR_OK) p.predicted_no_ec_us = po.predicted_us;
+  }
   *plan = p;
   return SPEAR_OK;
 }
