@@ -41,6 +41,12 @@ subset of the candidate layers enumerated under the documented grid rule;
 pinned by hand-worked instances, special cases, monotonicity in the slack and
 scipy's MILP solver on the same integer knapsack.
 
+The data-free EC initialisation (``oracle.spear_ec_init``): the rank-r
+truncated SVD of the quantization residual; pinned by the Eckart-Young error,
+the eigenvectors of E^T E (an independent algorithm), a residual of known
+singular structure, the balanced split, an exactly zero residual on a grid
+weight, and the falling gate-1 error as the rank grows.
+
 Parity unpinned: none of the functions here.  The quality claim of the
 abstract (perplexity-gap recovery) is outside this oracle.
 """
