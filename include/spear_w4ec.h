@@ -354,6 +354,33 @@ void spear_debug_fail_waits(int32_t on);
 spear_status_t spear_debug_stream_read(const void* src, size_t bytes, int32_t grid, void* sink, void* stream);
 
 /*
+ * spear_ec_init -- data-free initialisation of the EC factors: A B = the
+ * rank-r truncated SVD of the quantization residual E = W - dequant(Wq, s)
+ * (SPEAR page, abstract: lightweight compensators of the quantization error;
+ * SERQ page, "Saliency-Aware Low-Rank Error Reconstruction for LLM
+ * Quantization", Figure 1 and Table 8: a low-rank reconstruction of that error
+ * from its singular value decomposition).  The singular values are split
+ * evenly, A = U_r diag(sqrt(s)), B = diag(sqrt(s)) V_r^T, and each pair's sign
+ * makes the largest-magnitude entry of A's column positive.  Computed by
+ * randomized subspace iteration (rank + 16 columns, `iterations` rounds, 0 =
+ * 10) in fp32, with the small eigen-problems on the device.
+ *   W        fp16 [K, N] (the weight that was packed), 2-byte aligned.
+ *   Wq, scales  its packed form (spear_pack_w4: group_size 0; spear_pack_w4_grouped:
+ *            group_size SPEAR_GROUP_SIZE).
+ *   A        output fp16 [K, rank]; B output fp16 [rank, N] (2-byte aligned).
+ *   workspace  device memory of spear_ec_init_workspace_bytes (no clearing
+ *            needed; holds E in fp32, K N 4 bytes, and the iteration's blocks).
+ * rank <= 112 (the eigen-solver keeps rank + 16 columns in LDS): larger ranks
+ * are UNSUPPORTED.  A weight-preparation step, not part of the layer call.
+ * Errors: NULL_POINTER, INVALID_SHAPE, INVALID_ARGUMENT (iterations outside
+ *         [0, 64]), UNSUPPORTED, WORKSPACE_TOO_SMALL, MISALIGNED, HIP.
+ */
+spear_status_t spear_ec_init_workspace_bytes(int32_t K, int32_t N, int32_t rank, size_t* bytes);
+spear_status_t spear_ec_init(const void* W, const void* Wq, const void* scales, int32_t K, int32_t N,
+                             int32_t group_size, int32_t rank, int32_t iterations, void* A, void* B,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * spear_debug_unpack_w4 -- decode a packed weight back to int8 codes
  * q [K, N] (row-major, values in [-8, 7]) with the same in-register decode
  * the GEMM kernels use.  For bit-exactness tests.

@@ -26,6 +26,7 @@ __all__ = [
     "spear_w4ec_linear",
     "spear_ec_project",
     "spear_debug_unpack_w4",
+    "spear_ec_init",
     "spear_abi_version",
     "spear_take_error",
     "spear_w4ec_linear_noalloc",
@@ -94,6 +95,26 @@ def spear_pack_w4_grouped(W, group_size=128):
     st = library().spear_pack_w4_grouped(_ptr(W), K, N, int(group_size), _ptr(Wq), _ptr(s), _stream(W.device))
     _binding.check(st, "spear_pack_w4_grouped")
     return Wq, s
+
+
+def spear_ec_init(W, Wq, scales, rank, iterations=0):
+    """(A fp16 [K, r], B fp16 [r, N]): the rank-r truncated SVD of W's
+    quantization residual, on the GPU.  scales 1-D: per channel; 2-D: the
+    group scales of spear_pack_w4_grouped."""
+    _need(W, "W", torch.float16, 2)
+    _need(Wq, "Wq", torch.uint8, 1)
+    K, N = W.shape
+    group = 0 if scales.dim() == 1 else 128
+    nb = ctypes.c_size_t(0)
+    _binding.check(library().spear_ec_init_workspace_bytes(K, N, int(rank), ctypes.byref(nb)),
+                   "spear_ec_init_workspace_bytes")
+    ws = torch.empty(int(nb.value), dtype=torch.uint8, device=W.device)
+    A = torch.empty((K, rank), dtype=torch.float16, device=W.device)
+    B = torch.empty((rank, N), dtype=torch.float16, device=W.device)
+    st = library().spear_ec_init(_ptr(W), _ptr(Wq), _ptr(scales), K, N, group, int(rank), int(iterations), _ptr(A),
+                                 _ptr(B), _ptr(ws), ws.numel(), _stream(W.device))
+    _binding.check(st, "spear_ec_init")
+    return A, B
 
 
 def spear_debug_unpack_w4(Wq, K, N):

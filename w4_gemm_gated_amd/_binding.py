@@ -41,6 +41,8 @@ EXPORTS = (
     "spear_ec_workspace_bytes",
     "spear_ec_project",
     "spear_debug_unpack_w4",
+    "spear_ec_init_workspace_bytes",
+    "spear_ec_init",
     "spear_take_error",
     "spear_w4ec_linear_noalloc",
     "spear_debug_set_spin_limit",
@@ -133,6 +135,10 @@ def load(path=None):
     lib.spear_w4ec_linear_noalloc.restype = ctypes.c_int
     lib.spear_w4ec_linear_noalloc.argtypes = [ctypes.POINTER(LinearDesc), ctypes.POINTER(Plan),
                                               vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.spear_ec_init_workspace_bytes.restype = ctypes.c_int
+    lib.spear_ec_init_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
+    lib.spear_ec_init.restype = ctypes.c_int
+    lib.spear_ec_init.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.spear_take_error.restype = ctypes.c_int
     lib.spear_take_error.argtypes = [vp, sz, vp, vp]
     lib.spear_debug_set_spin_limit.restype = None

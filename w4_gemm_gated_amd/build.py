@@ -23,7 +23,7 @@ LIB_NAME = "libspear_w4ec.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "sched.cpp", "pack.hip", "ec_project.hip", "gemm.hip", "skinny.hip", "util.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "sched.cpp", "pack.hip", "ec_project.hip", "gemm.hip", "skinny.hip", "util.hip", "noalloc.hip", "ec_init.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -144,6 +144,37 @@ spear_status_t spear_pack_w4_grouped(const void* W, int32_t K, int32_t N, int32_
   return hip_status(launch_pack_w4_grouped(W, K, N, Wq, scales, stream));
 }
 
+spear_status_t spear_ec_init_workspace_bytes(int32_t K, int32_t N, int32_t rank, size_t* bytes) {
+  if (!bytes) return SPEAR_ERR_NULL_POINTER;
+  if (K < 8 || K % 8 != 0 || N < 1 || rank < 1 || rank > SPEAR_MAX_RANK) return SPEAR_ERR_INVALID_SHAPE;
+  const EcInitLayout L = ec_init_layout(K, N, rank);
+  if (!L.fits) return SPEAR_ERR_UNSUPPORTED;
+  *bytes = L.bytes;
+  return SPEAR_OK;
+}
+
+spear_status_t spear_ec_init(const void* W, const void* Wq, const void* scales, int32_t K, int32_t N,
+                             int32_t group_size, int32_t rank, int32_t iterations, void* A, void* B,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W || !Wq || !scales || !A || !B || !workspace) return SPEAR_ERR_NULL_POINTER;
+  if (K < 8 || K % 8 != 0 || N < 1 || rank < 1 || rank > SPEAR_MAX_RANK) return SPEAR_ERR_INVALID_SHAPE;
+  if (iterations < 0 || iterations > 64) return SPEAR_ERR_INVALID_ARGUMENT;
+  if (group_size != 0 && group_size != SPEAR_GROUP_SIZE) return SPEAR_ERR_UNSUPPORTED;
+  if ((int64_t)K * 8 > INT32_MAX || (int64_t)N * 16 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
+  const EcInitLayout L = ec_init_layout(K, N, rank);
+  if (!L.fits) return SPEAR_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.bytes) return SPEAR_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(W, 2) || !aligned(Wq, 16) || !aligned(scales, 2) || !aligned(A, 2) || !aligned(B, 2) ||
+      !aligned(workspace, 16))
+    return SPEAR_ERR_MISALIGNED;
+  EcInitArgs a;
+  a.W = W; a.Wq = Wq; a.scales = scales;
+  a.K = K; a.N = N; a.rank = rank; a.grouped = group_size != 0 ? 1 : 0;
+  a.iterations = iterations == 0 ? 10 : iterations;
+  a.A = A; a.B = B; a.workspace = workspace; a.layout = L;
+  return hip_status(launch_ec_init(a, stream));
+}
+
 spear_status_t spear_debug_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream) {
   if (!Wq || !q_out) return SPEAR_ERR_NULL_POINTER;
   if (K < 8 || K % 8 != 0 || N < 1) return SPEAR_ERR_INVALID_SHAPE;

@@ -193,6 +193,28 @@ hipError_t static_scratch(void** out, void* stream);
 hipError_t set_max_dynamic_lds(const void* kernel, int bytes);
 hipError_t launch_take_error(void* workspace, void* out, void* stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, int grid, void* sink, void* stream);
+// Data-free EC initialisation (ec_init.hip): workspace layout (byte offsets)
+// and launch arguments.
+struct EcInitLayout {
+  int l = 0;            // columns of the subspace iteration (rank + 16, even, <= 128)
+  int gram_parts = 1;   // row blocks of a Gram matrix's partial sums
+  size_t E = 0, Y = 0, Y2 = 0, V = 0, part = 0, G = 0, T = 0, evals = 0, A32 = 0, Bt32 = 0, sign = 0;
+  size_t bytes = 0;
+  bool fits = false;    // rank within what the eigen-solver's LDS holds
+};
+EcInitLayout ec_init_layout(int64_t K, int64_t N, int64_t rank);
+struct EcInitArgs {
+  const void* W;        // fp16 [K, N]
+  const void* Wq;       // packed codes (layout id 2)
+  const void* scales;   // per channel [N] or group [KC][N_pad]
+  int32_t K, N, rank, grouped, iterations;
+  void* A;              // fp16 [K, rank]
+  void* B;              // fp16 [rank, N]
+  void* workspace;
+  EcInitLayout layout;
+};
+hipError_t launch_ec_init(const EcInitArgs& a, void* stream);
+
 hipError_t launch_pack_w4(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_pack_w4_grouped(const void* W, int32_t K, int32_t N, void* Wq, void* scales, void* stream);
 hipError_t launch_unpack_w4(const void* Wq, int32_t K, int32_t N, void* q_out, void* stream);
