@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-mid", action="store_true", help="skip the mid-size-M configurations")
     ap.add_argument("--mid-steps", type=int, default=20)
     ap.add_argument("--no-grouped", action="store_true", help="skip the group-wise (g128) variant")
+    ap.add_argument("--no-ec-init", action="store_true", help="skip timing the data-free EC initialisation")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--pmc-mode", action="store_true",
@@ -416,6 +417,11 @@ def main():
     if not args.no_mid:
         scheduler = ec_scheduler_section(torch, sp, workloads, args.mid_steps, graph)
 
+    # ------------------------------------------------------------ EC initialisation
+    ec_init = None
+    if not args.no_ec_init:
+        ec_init = ec_init_section(torch, sp, workloads)
+
     # ------------------------------------------------------------ group-wise scales
     grouped = None
     if not args.no_grouped:
@@ -452,6 +458,7 @@ def main():
         "mid_m": mid,
         "g128": grouped,
         "ec_scheduler": scheduler,
+        "ec_init": ec_init,
         "cost_model": cost_model_report(sp, per_m, prefill, mid),
     }
     print(json.dumps(line), flush=True)
@@ -586,6 +593,33 @@ def grouped_section(torch, sp, workloads, steps, prefill_steps, graph, do_prefil
                                        "no_ec_us": round(t_off * 1e6, 2)}
         log(f"g128 prefill: {t_on * 1e6:.1f} us, EC off {t_off * 1e6:.1f} us")
         del pre, pYs
+    return out
+
+
+def ec_init_section(torch, sp, workloads):
+    """Time of the data-free EC initialisation (spear_ec_init, a weight-
+    preparation step) on the decode and prefill weights at their ranks: one
+    warm call, then the median of three; each call streams the fp32 residual
+    (4 K N bytes) twice per iteration (10) and once more, which gives the
+    effective rate beside the time."""
+    out = {}
+    for name, wid in (("decode_q_proj_4096x4096_r32", 2), ("prefill_up_proj_4096x14336_r64", 3)):
+        w = workloads.workload(wid)
+        W = torch.from_numpy(w["W"]).to("cuda:0")
+        Wq, s = sp.spear_pack_w4(W)
+        sp.spear_ec_init(W, Wq, s, w["r"])
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            sp.spear_ec_init(W, Wq, s, w["r"])
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        t = sorted(ts)[1]
+        streamed = (2 * 10 + 1) * 4 * w["K"] * w["N"]
+        out[name] = {"ms": round(t * 1e3, 2), "residual_stream_GB/s": round(streamed / t / 1e9, 1)}
+        log(f"ec_init {name}: {t * 1e3:.1f} ms")
+        del W, Wq, s
     return out
 
 
