@@ -221,16 +221,22 @@ PMC_COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_m16_hbm_traffic.json")
 
 
+# The sources that decide the decode call's code and launch: its kernel, the
+# headers it includes and the planner.
+DECODE_SOURCES = ("w4_gemm_gated_amd/csrc/skinny.hip", "w4_gemm_gated_amd/csrc/device_common.h",
+                  "w4_gemm_gated_amd/csrc/internal.h", "w4_gemm_gated_amd/csrc/plan.cpp",
+                  "include/spear_w4ec.h")
+
+
 def source_digest():
-    """Digest of the kernel sources, to tell whether stored counter readings
-    still describe the library as built."""
+    """Digest of the decode kernel's sources, to tell whether stored counter
+    readings still describe the library as built."""
     import hashlib
-    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "w4_gemm_gated_amd", "csrc")
+    root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(root)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(root, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(root, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
