@@ -363,14 +363,15 @@ spear_status_t spear_debug_stream_read(const void* src, size_t bytes, int32_t gr
  * evenly, A = U_r diag(sqrt(s)), B = diag(sqrt(s)) V_r^T, and each pair's sign
  * makes the largest-magnitude entry of A's column positive.  Computed by
  * randomized subspace iteration (rank + 16 columns, `iterations` rounds, 0 =
- * 10) in fp32, with the small eigen-problems on the device.
+ * 10) in fp32, each block orthonormalized by Cholesky QR applied twice, and a
+ * final Rayleigh-Ritz step whose small eigen-problem is solved on the device.
  *   W        fp16 [K, N] (the weight that was packed), 2-byte aligned.
  *   Wq, scales  its packed form (spear_pack_w4: group_size 0; spear_pack_w4_grouped:
  *            group_size SPEAR_GROUP_SIZE).
  *   A        output fp16 [K, rank]; B output fp16 [rank, N] (2-byte aligned).
  *   workspace  device memory of spear_ec_init_workspace_bytes (no clearing
  *            needed; holds E in fp32, K N 4 bytes, and the iteration's blocks).
- * rank <= 112 (the eigen-solver keeps rank + 16 columns in LDS): larger ranks
+ * rank <= 112 (the small solvers keep rank + 16 columns in LDS): larger ranks
  * are UNSUPPORTED.  A weight-preparation step, not part of the layer call.
  * Errors: NULL_POINTER, INVALID_SHAPE, INVALID_ARGUMENT (iterations outside
  *         [0, 64]), UNSUPPORTED, WORKSPACE_TOO_SMALL, MISALIGNED, HIP.

@@ -12,16 +12,18 @@
 //      per 128-row group);
 //   2. randomized subspace iteration with l = r + 16 columns: V0 from a
 //      counter hash, then `iterations` times Y = E V, orthonormalize, Z = E^T Y,
-//      orthonormalize -> V; each orthonormalization is Y <- Y W L^-1/2 from the
-//      eigen-decomposition Y^T Y = W L W^T, applied twice (the second pass
-//      mends what fp32 loses on a poorly conditioned block);
+//      orthonormalize -> V; each orthonormalization is Y <- Y L^-T from the
+//      Cholesky factor Y^T Y = L L^T, applied twice (CholeskyQR2: the second
+//      pass mends what fp32 loses on a poorly conditioned block);
 //   3. Rayleigh-Ritz: Y = E V, Y^T Y = W L W^T (eigenvalues descending),
 //      s_j = sqrt(L_j), A = Y W_r diag(s^-1/2), B^T = V W_r diag(s^1/2);
 //   4. each singular pair's sign so that the largest-magnitude entry of A's
 //      column is positive (ties: the lowest row), then fp16 A [K][r], B [r][N].
-// Eigen-decompositions: parallel cyclic Jacobi on one workgroup, the l x l
-// matrix and its eigenvectors in LDS (l <= 128), round-robin pairing so the
-// l/2 rotations of a step touch disjoint rows and columns.
+// Products (E V, E^T Y, Gram matrices, basis changes) share one tiled fp32
+// kernel, K-split where its tiles alone would not fill the CUs.  The Cholesky
+// factor and the eigen-decomposition of the l x l Gram matrices run on one
+// workgroup each, in LDS (l <= 128): Cholesky by columns, the eigenpairs by
+// parallel cyclic Jacobi.
 #include <algorithm>
 #include <cmath>
 
@@ -76,130 +78,196 @@ __global__ void ec_start_kernel(float* V, int64_t count) {
 }
 
 // -------------------------------------------------------------- products
-// C[R][l] = op(E) D[L][l] with op(E) = E [R][L] (TRANS false, E stored
-// [R][L]) or E^T (TRANS true, E stored [L][R]).  A workgroup owns 64 rows of
-// C; per 64-wide slice of the inner dimension the E tile (64 x 64) and the D
-// slice (64 x l) go through LDS; thread t computes row t % 64 of C for the
-// columns c = t / 64 + 4 i.
+// C[R][n] = op(E) D with op(E) = E [R][L] (TRANS false, E stored [R][L]) or
+// E^T (TRANS true, E stored [L][R]) and D [L][n], n <= 128.  Workgroup
+// (x, y, z) owns rows 64x.., columns 64y.. of C and the z-th range of
+// `slices` 64-wide steps of the inner dimension (a K split: each range writes
+// its own partial C, summed afterwards in fixed order).  Per step the E tile
+// (held k-major, et[k][row]) and the D tile (dt[k][col]) go through LDS, the
+// next step's tiles are loaded into registers meanwhile, and thread t computes
+// a 4 x 4 block of C: rows 4 (t / 16).., columns 4 (t % 16)...
+constexpr int kEtStride = kTile + 1;   // transposing E stores (TRANS false) conflict-free
+
 template <bool TRANS>
 __global__ void __launch_bounds__(kEiThreads)
-ec_product_kernel(const float* __restrict__ E, const float* __restrict__ D, float* __restrict__ C, int R, int L, int l) {
-  __shared__ float et[kTile][kTile + 1];
-  __shared__ float dt[kTile][kMaxL];
-  const int tid = threadIdx.x, r_loc = tid % kTile, cg = tid / kTile;
-  const int r0 = blockIdx.x * kTile;
-  float acc[kMaxL / 4];
+ec_mm_kernel(const float* __restrict__ E, const float* __restrict__ D, float* __restrict__ C, int R, int L, int n,
+             int slices) {
+  __shared__ float et[kTile * kEtStride];
+  __shared__ __align__(16) float dt[kTile * kTile];
+  const int tid = threadIdx.x;
+  const int r0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
+  const int k_first = blockIdx.z * slices * kTile;
+  const int k_end = min(L, k_first + slices * kTile);
+  C += (size_t)blockIdx.z * R * n;
+  // Loads: element i of the 4096 in a tile is (a = i / 64, b = i % 64); lanes
+  // run along b, which is contiguous in memory for both operands.
+  float er[16], dr[16];
+  auto load = [&](int k0) {
 #pragma unroll
-  for (int i = 0; i < kMaxL / 4; ++i) acc[i] = 0.0f;
-  for (int c0 = 0; c0 < L; c0 += kTile) {
-    // E tile: et[row][inner]
-    for (int idx = tid; idx < kTile * kTile; idx += kEiThreads) {
-      const int a = idx / kTile, b = idx % kTile;      // coalesced along b
-      float v = 0.0f;
-      if (!TRANS) {
-        const int row = r0 + a, in = c0 + b;
-        if (row < R && in < L) v = E[(size_t)row * L + in];
-        et[a][b] = v;
-      } else {
-        const int in = c0 + a, row = r0 + b;
-        if (row < R && in < L) v = E[(size_t)in * R + row];
-        et[b][a] = v;
+    for (int u = 0; u < 16; ++u) {
+      const int i = tid + u * kEiThreads, a = i / kTile, b = i % kTile;
+      if (!TRANS) {            // E[row = r0 + a][k = k0 + b]
+        const int row = r0 + a, k = k0 + b;
+        er[u] = (row < R && k < k_end) ? E[(size_t)row * L + k] : 0.0f;
+      } else {                 // E[k = k0 + a][row = r0 + b]
+        const int k = k0 + a, row = r0 + b;
+        er[u] = (row < R && k < k_end) ? E[(size_t)k * R + row] : 0.0f;
       }
+      const int k = k0 + a, c = c0 + b;
+      dr[u] = (k < k_end && c < n) ? D[(size_t)k * n + c] : 0.0f;
     }
-    for (int idx = tid; idx < kTile * l; idx += kEiThreads) {
-      const int a = idx / l, b = idx % l;
-      dt[a][b] = c0 + a < L ? D[(size_t)(c0 + a) * l + b] : 0.0f;
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = tid + u * kEiThreads, a = i / kTile, b = i % kTile;
+      if (!TRANS) et[b * kEtStride + a] = er[u];
+      else et[a * kEtStride + b] = er[u];
+      dt[a * kTile + b] = dr[u];
     }
+  };
+  const int tr = tid / 16, tc = tid % 16;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  if (k_first < k_end) load(k_first);
+  for (int k0 = k_first; k0 < k_end; k0 += kTile) {
     __syncthreads();
+    store();
+    __syncthreads();
+    if (k0 + kTile < k_end) load(k0 + kTile);
+#pragma unroll 8
     for (int k = 0; k < kTile; ++k) {
-      const float e = et[r_loc][k];
+      float av[4];
 #pragma unroll
-      for (int i = 0; i < kMaxL / 4; ++i) {
-        const int c = cg + 4 * i;
-        if (c < l) acc[i] = fmaf(e, dt[k][c], acc[i]);
+      for (int i = 0; i < 4; ++i) av[i] = et[k * kEtStride + tr * 4 + i];
+      const float4 bv = *reinterpret_cast<const float4*>(&dt[k * kTile + tc * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i][0] = fmaf(av[i], bv.x, acc[i][0]);
+        acc[i][1] = fmaf(av[i], bv.y, acc[i][1]);
+        acc[i][2] = fmaf(av[i], bv.z, acc[i][2]);
+        acc[i][3] = fmaf(av[i], bv.w, acc[i][3]);
       }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = r0 + tr * 4 + i;
+    if (row >= R) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + tc * 4 + j;
+      if (c < n) C[(size_t)row * n + c] = acc[i][j];
+    }
+  }
+}
+
+// C[i] = sum over the `parts` partial results part[p][i], in order of p.
+__global__ void ec_reduce_kernel(const float* __restrict__ part, int parts, int64_t count, float* __restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float s = 0.0f;
+  for (int p = 0; p < parts; ++p) s += part[(size_t)p * count + i];
+  C[i] = s;
+}
+
+// -------------------------------------------------------------- Cholesky QR
+// T = L^-T from the Cholesky factor of the Gram matrix G = Y^T Y = L L^T
+// (l x l, one workgroup, in LDS), so that Y T has orthonormal columns: one
+// pass of Cholesky QR (applied twice, it is CholeskyQR2: Fukaya, Nakatsukasa,
+// Yanagisawa and Yamamoto, "CholeskyQR2: a simple and communication-avoiding
+// algorithm for computing a tall-skinny QR factorization", 2014).  A column
+// whose pivot is not above 1e-12 of the largest diagonal entry (a direction
+// the block does not span: a zero or rank-deficient residual) is dropped: its
+// column of L is zeroed and its column of T is zero.
+__global__ void __launch_bounds__(kEiThreads) ec_cholinv_kernel(const float* __restrict__ G, int l, float* __restrict__ T) {
+  extern __shared__ float sm[];
+  float* a = sm;                        // [l][l]: G, then L in the lower triangle
+  float* x = sm + l * l;                // [l][l]: X = L^-1, column c owned by thread c
+  __shared__ float red[kEiThreads];
+  __shared__ int keep[kMaxL];
+  const int tid = threadIdx.x;
+  float dm = 0.0f;
+  for (int e = tid; e < l * l; e += kEiThreads) {
+    a[e] = G[e];
+    if (e / l == e % l) dm = fmaxf(dm, G[e]);
+  }
+  red[tid] = dm;
+  __syncthreads();
+  for (int st = kEiThreads / 2; st > 0; st /= 2) {
+    if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
+    __syncthreads();
+  }
+  const float tol = 1e-12f * red[0];
+  for (int j = 0; j < l; ++j) {
+    const float d = a[j * l + j];
+    const bool ok = d > tol && d > 0.0f;
+    const float piv = ok ? sqrtf(d) : 0.0f;
+    const float inv = ok ? 1.0f / piv : 0.0f;
+    // column j below the diagonal, then the trailing lower triangle
+    for (int i = j + 1 + tid; i < l; i += kEiThreads) a[i * l + j] *= inv;
+    __syncthreads();
+    const int m = l - j - 1;
+    for (int e = tid; e < m * m; e += kEiThreads) {
+      const int i = j + 1 + e / m, k = j + 1 + e % m;
+      if (k <= i) a[i * l + k] = fmaf(-a[i * l + j], a[k * l + j], a[i * l + k]);
+    }
+    if (tid == 0) {
+      a[j * l + j] = piv;
+      keep[j] = ok;
     }
     __syncthreads();
   }
-  const int row = r0 + r_loc;
-  if (row < R) {
-#pragma unroll
-    for (int i = 0; i < kMaxL / 4; ++i) {
-      const int c = cg + 4 * i;
-      if (c < l) C[(size_t)row * l + c] = acc[i];
+  // X = L^-1 by forward substitution, one column per thread.
+  for (int c = tid; c < l; c += kEiThreads) {
+    for (int i = 0; i < l; ++i) {
+      float v = 0.0f;
+      if (i == c) v = keep[i] ? 1.0f / a[i * l + i] : 0.0f;
+      else if (i > c && keep[i]) {
+        float s = 0.0f;
+        for (int k = c; k < i; ++k) s = fmaf(a[i * l + k], x[k * l + c], s);
+        v = -s / a[i * l + i];
+      }
+      x[i * l + c] = v;
     }
   }
-}
-
-// Out[R][c] = In[R][l] T[l][c] (T [l][c] with c <= l, in LDS); one thread per row.
-__global__ void __launch_bounds__(kEiThreads)
-ec_apply_kernel(const float* __restrict__ In, const float* __restrict__ T, float* __restrict__ Out, int R, int l, int c) {
-  __shared__ float ts[kMaxL * kMaxL];
-  for (int idx = threadIdx.x; idx < l * c; idx += kEiThreads) ts[idx] = T[idx];
   __syncthreads();
-  const int row = blockIdx.x * kEiThreads + threadIdx.x;
-  if (row >= R) return;
-  float x[kMaxL];
-#pragma unroll
-  for (int i = 0; i < kMaxL; ++i) x[i] = i < l ? In[(size_t)row * l + i] : 0.0f;
-  for (int j = 0; j < c; ++j) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxL; ++i)
-      if (i < l) s = fmaf(x[i], ts[i * c + j], s);
-    Out[(size_t)row * c + j] = s;
-  }
-}
-
-// Gram matrix G = Y^T Y of Y [R][l]: workgroup b sums rows [b * rows_per, ...)
-// into part[b][l][l]; the sum over workgroups is taken in fixed order.
-__global__ void __launch_bounds__(kEiThreads)
-ec_gram_part_kernel(const float* __restrict__ Y, int R, int l, int rows_per, float* __restrict__ part) {
-  const int b = blockIdx.x;
-  const int rbeg = b * rows_per, rend = min(R, rbeg + rows_per);
-  for (int e = threadIdx.x; e < l * l; e += kEiThreads) {
-    const int i = e / l, j = e % l;
-    float s = 0.0f;
-    if (i <= j)
-      for (int r = rbeg; r < rend; ++r) s = fmaf(Y[(size_t)r * l + i], Y[(size_t)r * l + j], s);
-    part[(size_t)b * l * l + e] = s;
-  }
-}
-__global__ void ec_gram_sum_kernel(const float* __restrict__ part, int parts, int l, float* __restrict__ G) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= l * l) return;
-  const int i = e / l, j = e % l;
-  const int src = i <= j ? e : j * l + i;                 // the upper triangle, mirrored
-  float s = 0.0f;
-  for (int b = 0; b < parts; ++b) s += part[(size_t)b * l * l + src];
-  G[e] = s;
+  // T = X^T
+  for (int e = tid; e < l * l; e += kEiThreads) T[e] = x[(e % l) * l + e / l];
 }
 
 // -------------------------------------------------------------- Jacobi
-// Eigen-decomposition of the symmetric G [l][l] (l even, <= 128): cyclic
-// Jacobi with round-robin pairs.  Output: the transform T [l][c] for one of
-// three uses, with the eigenpairs ordered by decreasing eigenvalue:
-//   mode 0 (orthonormalize): T = W diag(L^-1/2), c = l, eigenvalues below
-//          1e-12 of the largest give zero columns;
-//   mode 1 (factor A):       T = W_r diag(L_r^-1/4), c = r;
-//   mode 2 (factor B^T):     T = W_r diag(L_r^+1/4), c = r.
-// (L_j = s_j^2, so L^-1/4 = s^-1/2 and L^+1/4 = s^+1/2.)
+// Rayleigh-Ritz step: eigen-decomposition of the symmetric G [l][l] (l even,
+// <= 128) by cyclic Jacobi, with the l/2 rotations of a step on disjoint
+// row/column pairs (the round-robin "circle" schedule: index l - 1 fixed,
+// the others rotating, so l - 1 steps pair every two indexes once).  Outputs,
+// eigenpairs ordered by decreasing eigenvalue L_j = s_j^2:
+//   TA = W_r diag(L_r^-1/4) [l][r]   (A = Y TA)
+//   TB = W_r diag(L_r^+1/4) [l][r]   (B^T = V TB)
+// and the eigenvalues.  Eigenvalues not above 1e-12 of the largest give zero
+// columns.
 __global__ void __launch_bounds__(kEiThreads)
-ec_jacobi_kernel(const float* __restrict__ G, int l, int mode, int r, float* __restrict__ T, float* __restrict__ evals) {
+ec_jacobi_kernel(const float* __restrict__ G, int l, int r, float* __restrict__ TA, float* __restrict__ TB,
+                 float* __restrict__ evals) {
   extern __shared__ float sm[];
   float* a = sm;                        // [l][l]
   float* v = sm + l * l;                // [l][l] eigenvectors (columns)
   float* cs = v + l * l;                // [l/2][2] rotation c, s
-  int* pr = reinterpret_cast<int*>(cs + l);     // [l] current round-robin order
-  int* ord = pr + l;                             // [l] eigenpair order
+  int* ord = reinterpret_cast<int*>(cs + l);     // [l] eigenpair order
   __shared__ float red[kEiThreads];
-  const int tid = threadIdx.x, half = l / 2;
+  const int tid = threadIdx.x, half = l / 2, m = l - 1;
   for (int e = tid; e < l * l; e += kEiThreads) {
     a[e] = G[e];
     v[e] = (e / l == e % l) ? 1.0f : 0.0f;
   }
-  for (int i = tid; i < l; i += kEiThreads) pr[i] = i;
   __syncthreads();
+  auto pair = [&](int step, int k, int& p, int& q) {
+    if (k == 0) { p = step; q = m; }
+    else { p = (step + k) % m; q = (step - k + m) % m; }
+  };
   for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
     // Off-diagonal and diagonal norms: stop when the off part is negligible.
     float off = 0.0f, dia = 0.0f;
@@ -224,10 +292,10 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int mode, int r, float* __r
     const float dia_all = red[0];
     __syncthreads();
     if (!(off_all > 1e-14f * dia_all)) break;
-    for (int step = 0; step < l - 1; ++step) {
-      // pairs k: (pr[k], pr[l - 1 - k])
+    for (int step = 0; step < m; ++step) {
       for (int k = tid; k < half; k += kEiThreads) {
-        const int p = pr[k], q = pr[l - 1 - k];
+        int p, q;
+        pair(step, k, p, q);
         const float apq = a[p * l + q], app = a[p * l + p], aqq = a[q * l + q];
         float c = 1.0f, s = 0.0f;
         if (fabsf(apq) > 1e-30f) {
@@ -243,7 +311,8 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int mode, int r, float* __r
       // columns p, q of a and v:  (x_p, x_q) <- (c x_p - s x_q, s x_p + c x_q)
       for (int e = tid; e < half * l; e += kEiThreads) {
         const int k = e / l, i = e % l;
-        const int p = pr[k], q = pr[l - 1 - k];
+        int p, q;
+        pair(step, k, p, q);
         const float c = cs[2 * k], s = cs[2 * k + 1];
         const float xp = a[i * l + p], xq = a[i * l + q];
         a[i * l + p] = c * xp - s * xq;
@@ -256,18 +325,12 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int mode, int r, float* __r
       // rows p, q of a
       for (int e = tid; e < half * l; e += kEiThreads) {
         const int k = e / l, j = e % l;
-        const int p = pr[k], q = pr[l - 1 - k];
+        int p, q;
+        pair(step, k, p, q);
         const float c = cs[2 * k], s = cs[2 * k + 1];
         const float xp = a[p * l + j], xq = a[q * l + j];
         a[p * l + j] = c * xp - s * xq;
         a[q * l + j] = s * xp + c * xq;
-      }
-      __syncthreads();
-      // next round-robin order: position 0 fixed, the others rotate by one
-      if (tid == 0) {
-        const int last = pr[l - 1];
-        for (int i = l - 1; i > 1; --i) pr[i] = pr[i - 1];
-        pr[1] = last;
       }
       __syncthreads();
     }
@@ -285,16 +348,13 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int mode, int r, float* __r
   __syncthreads();
   float lmax = 0.0f;
   for (int j = 0; j < l; ++j) lmax = fmaxf(lmax, a[j * l + j]);
-  const int c = mode == 0 ? l : r;
-  for (int e = tid; e < l * c; e += kEiThreads) {
-    const int i = e / c, jj = e % c;
+  for (int e = tid; e < l * r; e += kEiThreads) {
+    const int i = e / r, jj = e % r;
     const int src = ord[jj];
     const float lam = a[src * l + src];
-    float f = 0.0f;
-    if (lam > 1e-12f * lmax && lam > 0.0f) {
-      f = mode == 0 ? rsqrtf(lam) : mode == 1 ? rsqrtf(sqrtf(lam)) : sqrtf(sqrtf(lam));
-    }
-    T[e] = v[i * l + src] * f;
+    const bool ok = lam > 1e-12f * lmax && lam > 0.0f;
+    TA[e] = ok ? v[i * l + src] * rsqrtf(sqrtf(lam)) : 0.0f;
+    TB[e] = ok ? v[i * l + src] * sqrtf(sqrtf(lam)) : 0.0f;
   }
   if (evals)
     for (int jj = tid; jj < l; jj += kEiThreads) evals[jj] = a[ord[jj] * l + ord[jj]];
@@ -340,21 +400,50 @@ __global__ void ec_write_kernel(const float* __restrict__ A32, const float* __re
 
 }  // namespace
 
+namespace {
+
+constexpr int64_t kTargetGroups = 512;   // workgroups a product aims for (two per CU)
+constexpr int64_t kMaxParts = 128;       // K-split ranges of one product at most
+
+// K split of the product C[R][n] = op(E) D over an inner extent L: `slices`
+// 64-wide steps per range, `parts` ranges.
+struct MmSplit {
+  int slices, parts;
+};
+MmSplit mm_split(int64_t R, int64_t L, int64_t n) {
+  const int64_t steps = std::max<int64_t>(1, ceil_div(L, kTile));
+  const int64_t tiles = ceil_div(R, kTile) * ceil_div(n, kTile);
+  const int64_t want = std::max<int64_t>(1, std::min({steps, kMaxParts, ceil_div(kTargetGroups, tiles)}));
+  const int64_t slices = ceil_div(steps, want);
+  return {(int)slices, (int)ceil_div(steps, slices)};
+}
+size_t mm_part_floats(int64_t R, int64_t L, int64_t n) {
+  const MmSplit p = mm_split(R, L, n);
+  return p.parts > 1 ? (size_t)p.parts * R * n : 0;
+}
+
+}  // namespace
+
 EcInitLayout ec_init_layout(int64_t K, int64_t N, int64_t rank) {
   EcInitLayout L;
   L.l = (int)round_up(std::min<int64_t>(rank + kOversample, std::min(K, N)), 2);
   if (L.l > std::min(K, N)) L.l -= 2;
-  L.gram_parts = (int)std::min<int64_t>(64, ceil_div(std::max(K, N), 256));
+  const int64_t l = L.l;
+  // partial sums of the largest split product
+  const size_t part = std::max({mm_part_floats(K, N, l), mm_part_floats(N, K, l), mm_part_floats(l, K, l),
+                                mm_part_floats(l, N, l), mm_part_floats(K, l, l), mm_part_floats(N, l, l),
+                                mm_part_floats(K, l, rank), mm_part_floats(N, l, rank), (size_t)1});
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = (size_t)round_up((int64_t)(off + bytes), 256); return o; };
   L.E = take((size_t)K * N * 4);
-  L.Y = take((size_t)K * L.l * 4);
-  L.Y2 = take((size_t)std::max(K, N) * L.l * 4);
-  L.V = take((size_t)N * L.l * 4);
-  L.part = take((size_t)L.gram_parts * L.l * L.l * 4);
-  L.G = take((size_t)L.l * L.l * 4);
-  L.T = take((size_t)L.l * L.l * 4);
-  L.evals = take((size_t)L.l * 4);
+  L.Y = take((size_t)K * l * 4);
+  L.Y2 = take((size_t)std::max(K, N) * l * 4);
+  L.V = take((size_t)N * l * 4);
+  L.part = take(part * 4);
+  L.G = take((size_t)l * l * 4);
+  L.T = take((size_t)l * l * 4);
+  L.T2 = take((size_t)l * l * 4);
+  L.evals = take((size_t)l * 4);
   L.A32 = take((size_t)K * rank * 4);
   L.Bt32 = take((size_t)N * rank * 4);
   L.sign = take((size_t)rank * 4);
@@ -374,57 +463,62 @@ hipError_t launch_ec_init(const EcInitArgs& a, void* stream) {
   float* part = (float*)(ws + L.part);
   float* G = (float*)(ws + L.G);
   float* T = (float*)(ws + L.T);
+  float* T2 = (float*)(ws + L.T2);
   float* A32 = (float*)(ws + L.A32);
   float* Bt32 = (float*)(ws + L.Bt32);
   float* sign = (float*)(ws + L.sign);
   const int K = a.K, N = a.N, l = L.l, r = a.rank;
   const int KC = (int)(k_pad(K) / kKChunk), NP = (int)n_pad(N);
-  const size_t jacobi_lds = (size_t)2 * l * l * 4 + (size_t)l * 4 + (size_t)2 * l * 4;
+  const size_t chol_lds = (size_t)2 * l * l * 4;
+  const size_t jacobi_lds = (size_t)2 * l * l * 4 + (size_t)2 * l * 4;
   hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ec_jacobi_kernel), (int)jacobi_lds);
+  if (e == hipSuccess) e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ec_cholinv_kernel), (int)chol_lds);
   if (e != hipSuccess) return e;
+  // C[R][n] = op(E) D, K-split into the partial-sum buffer where that fills the CUs.
+  auto mm = [&](bool trans, const float* Ein, const float* D, float* C, int R, int Lin, int n) {
+    const MmSplit p = mm_split(R, Lin, n);
+    float* out = p.parts > 1 ? part : C;
+    const dim3 grid((unsigned)ceil_div(R, kTile), (unsigned)ceil_div(n, kTile), (unsigned)p.parts);
+    if (trans)
+      hipLaunchKernelGGL(ec_mm_kernel<true>, grid, dim3(kEiThreads), 0, s, Ein, D, out, R, Lin, n, p.slices);
+    else
+      hipLaunchKernelGGL(ec_mm_kernel<false>, grid, dim3(kEiThreads), 0, s, Ein, D, out, R, Lin, n, p.slices);
+    if (p.parts > 1) {
+      const int64_t count = (int64_t)R * n;
+      hipLaunchKernelGGL(ec_reduce_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, part, p.parts, count,
+                         C);
+    }
+  };
   const int64_t words = (int64_t)(K / 8) * N;
   hipLaunchKernelGGL(ec_residual_kernel, dim3((unsigned)ceil_div(words, kEiThreads)), dim3(kEiThreads), 0, s,
                      (const half_t*)a.W, (const uint32_t*)a.Wq, (const half_t*)a.scales, K, N, KC, NP, a.grouped, E);
   hipLaunchKernelGGL(ec_start_kernel, dim3((unsigned)ceil_div((int64_t)N * l, 256)), dim3(256), 0, s, V,
                      (int64_t)N * l);
-  // X <- X W L^-1/2 twice, for a block of R rows held in X: the first pass
-  // writes the scratch block Y2, the second writes X again.
+  // X [R][l] <- X L^-T twice (CholeskyQR2): the first pass writes the scratch
+  // block Y2, the second writes X again.
   auto orthonormalize = [&](float* X, int R) {
-    const int rows_per = (int)ceil_div(R, L.gram_parts);
-    const int parts = (int)ceil_div(R, rows_per);
     for (int pass = 0; pass < 2; ++pass) {
       const float* src = pass == 0 ? X : Y2;
       float* dst = pass == 0 ? Y2 : X;
-      hipLaunchKernelGGL(ec_gram_part_kernel, dim3(parts), dim3(kEiThreads), 0, s, src, R, l, rows_per, part);
-      hipLaunchKernelGGL(ec_gram_sum_kernel, dim3((unsigned)ceil_div(l * l, 256)), dim3(256), 0, s, part, parts, l, G);
-      hipLaunchKernelGGL(ec_jacobi_kernel, dim3(1), dim3(kEiThreads), jacobi_lds, s, G, l, 0, l, T, (float*)nullptr);
-      hipLaunchKernelGGL(ec_apply_kernel, dim3((unsigned)ceil_div(R, kEiThreads)), dim3(kEiThreads), 0, s, src, T, dst,
-                         R, l, l);
+      mm(true, src, src, G, l, R, l);
+      hipLaunchKernelGGL(ec_cholinv_kernel, dim3(1), dim3(kEiThreads), chol_lds, s, G, l, T);
+      mm(false, src, T, dst, R, l, l);
     }
   };
   orthonormalize(V, N);
   for (int it = 0; it < a.iterations; ++it) {
-    hipLaunchKernelGGL(ec_product_kernel<false>, dim3((unsigned)ceil_div(K, kTile)), dim3(kEiThreads), 0, s, E, V, Y, K,
-                       N, l);
+    mm(false, E, V, Y, K, N, l);
     orthonormalize(Y, K);
-    hipLaunchKernelGGL(ec_product_kernel<true>, dim3((unsigned)ceil_div(N, kTile)), dim3(kEiThreads), 0, s, E, Y, V, N,
-                       K, l);
+    mm(true, E, Y, V, N, K, l);
     orthonormalize(V, N);
   }
   // Rayleigh-Ritz on the final basis V.
-  hipLaunchKernelGGL(ec_product_kernel<false>, dim3((unsigned)ceil_div(K, kTile)), dim3(kEiThreads), 0, s, E, V, Y, K, N,
-                     l);
-  {
-    const int rows_per = (int)ceil_div(K, L.gram_parts);
-    const int parts = (int)ceil_div(K, rows_per);
-    hipLaunchKernelGGL(ec_gram_part_kernel, dim3(parts), dim3(kEiThreads), 0, s, Y, K, l, rows_per, part);
-    hipLaunchKernelGGL(ec_gram_sum_kernel, dim3((unsigned)ceil_div(l * l, 256)), dim3(256), 0, s, part, parts, l, G);
-  }
-  hipLaunchKernelGGL(ec_jacobi_kernel, dim3(1), dim3(kEiThreads), jacobi_lds, s, G, l, 1, r, T,
+  mm(false, E, V, Y, K, N, l);
+  mm(true, Y, Y, G, l, K, l);
+  hipLaunchKernelGGL(ec_jacobi_kernel, dim3(1), dim3(kEiThreads), jacobi_lds, s, G, l, r, T, T2,
                      (float*)(ws + L.evals));
-  hipLaunchKernelGGL(ec_apply_kernel, dim3((unsigned)ceil_div(K, kEiThreads)), dim3(kEiThreads), 0, s, Y, T, A32, K, l, r);
-  hipLaunchKernelGGL(ec_jacobi_kernel, dim3(1), dim3(kEiThreads), jacobi_lds, s, G, l, 2, r, T, (float*)nullptr);
-  hipLaunchKernelGGL(ec_apply_kernel, dim3((unsigned)ceil_div(N, kEiThreads)), dim3(kEiThreads), 0, s, V, T, Bt32, N, l, r);
+  mm(false, Y, T, A32, K, l, r);
+  mm(false, V, T2, Bt32, N, l, r);
   hipLaunchKernelGGL(ec_sign_kernel, dim3(r), dim3(kEiThreads), 0, s, A32, K, r, sign);
   const int64_t outs = std::max((int64_t)K * r, (int64_t)r * N);
   hipLaunchKernelGGL(ec_write_kernel, dim3((unsigned)ceil_div(outs, 256)), dim3(256), 0, s, A32, Bt32, sign, K, N, r,

@@ -197,8 +197,7 @@ hipError_t launch_stream_read(const void* src, size_t bytes, int grid, void* sin
 // and launch arguments.
 struct EcInitLayout {
   int l = 0;            // columns of the subspace iteration (rank + 16, even, <= 128)
-  int gram_parts = 1;   // row blocks of a Gram matrix's partial sums
-  size_t E = 0, Y = 0, Y2 = 0, V = 0, part = 0, G = 0, T = 0, evals = 0, A32 = 0, Bt32 = 0, sign = 0;
+  size_t E = 0, Y = 0, Y2 = 0, V = 0, part = 0, G = 0, T = 0, T2 = 0, evals = 0, A32 = 0, Bt32 = 0, sign = 0;
   size_t bytes = 0;
   bool fits = false;    // rank within what the eigen-solver's LDS holds
 };
