@@ -171,7 +171,8 @@ spear_status_t spear_pack_w4_grouped(const void* W, int32_t K, int32_t N, int32_
  * producers = 0, no workspace); otherwise producer workgroups lead the grid
  * and hand P and the gate over through the workspace (ec_local = 0).  FUSED with
  * rank % 4 != 0 (or with more than 4096 row tiles of 64 in the tiled case),
- * and the tiled kernel (M > 16) with X or the packed weight above
+ * the skinny kernel (M <= 16) with K above 262144 (64 K splits of 32 chunks of
+ * 128), and the tiled kernel (M > 16) with X or the packed weight above
  * 2^31 - 1 bytes (32-bit buffer offsets), are UNSUPPORTED.  The per-token gate-value
  * decision (skip the EC term of a tile whose gates are all below tau) is
  * taken on the device inside the epilogue, so no gate value ever crosses to
@@ -371,8 +372,9 @@ spear_status_t spear_debug_stream_read(const void* src, size_t bytes, int32_t gr
  *   A        output fp16 [K, rank]; B output fp16 [rank, N] (2-byte aligned).
  *   workspace  device memory of spear_ec_init_workspace_bytes (no clearing
  *            needed; holds E in fp32, K N 4 bytes, and the iteration's blocks).
- * rank <= 112 (the small solvers keep rank + 16 columns in LDS): larger ranks
- * are UNSUPPORTED.  A weight-preparation step, not part of the layer call.
+ * rank <= 112 (the small solvers keep rank + 16 columns in LDS): larger ranks,
+ * and K above 2^28 - 1 or N above 2^27 - 1, are UNSUPPORTED (also by
+ * spear_ec_init_workspace_bytes).  A weight-preparation step, not part of the layer call.
  * Errors: NULL_POINTER, INVALID_SHAPE, INVALID_ARGUMENT (iterations outside
  *         [0, 64]), UNSUPPORTED, WORKSPACE_TOO_SMALL, MISALIGNED, HIP.
  */

@@ -174,6 +174,22 @@ def test_dispatch_rejects_bad_shapes(lib, M, K, N, r, code):
     assert plan(lib, M, K, N, r)[0] == code
 
 
+def test_dispatch_limits_of_the_kernels(lib):
+    """Shapes the kernels cannot run are UNSUPPORTED, never a plan of zero
+    workgroups: the decode kernel takes K up to 64 splits of 32 chunks of 128,
+    and a launch stays within 2^30 workgroups."""
+    st, p = plan(lib, 16, 262144, 512, 0)
+    assert st == 0 and p.kernel == 0 and p.grid >= 1
+    assert plan(lib, 16, 262144 + 128, 512, 0)[0] == 3
+    assert plan(lib, 1, 1 << 24, 16, 0)[0] == 3
+    assert plan(lib, 1 << 24, 8, 1 << 24, 0)[0] == 3
+    nb = ctypes.c_size_t(0)
+    assert lib.spear_ec_init_workspace_bytes(2147483640, 2147483647, 32, ctypes.byref(nb)) == 3
+    assert lib.spear_ec_init_workspace_bytes(8, 1, 1, ctypes.byref(nb)) == 3     # l = 0 < rank
+    assert lib.spear_ec_init_workspace_bytes(4096, 4096, 32, ctypes.byref(nb)) == 0
+    assert nb.value >= 4096 * 4096 * 4
+
+
 def test_dispatch_rejects_bad_arguments(lib):
     assert plan(lib, 16, 512, 512, 16, variant=7)[0] == 8
     assert plan(lib, 16, 512, 512, 16, bias=float("nan"))[0] == 8

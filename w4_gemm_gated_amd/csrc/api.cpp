@@ -102,7 +102,12 @@ hipError_t set_max_dynamic_lds(const void* kernel, int bytes) {
 
 extern "C" {
 
-const char* spear_status_str(spear_status_t s) {
+const char* spear_status_str(spear_status_t status) {
+  // A C caller may pass any int; read it as one (an out-of-range value held
+  // in the C++ enum type would be undefined behaviour).
+  int32_t s;
+  static_assert(sizeof s == sizeof status, "spear_status_t is an int");
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case SPEAR_OK: return "SPEAR_OK";
     case SPEAR_ERR_NULL_POINTER: return "SPEAR_ERR_NULL_POINTER: a required pointer is NULL";
@@ -147,6 +152,7 @@ spear_status_t spear_pack_w4_grouped(const void* W, int32_t K, int32_t N, int32_
 spear_status_t spear_ec_init_workspace_bytes(int32_t K, int32_t N, int32_t rank, size_t* bytes) {
   if (!bytes) return SPEAR_ERR_NULL_POINTER;
   if (K < 8 || K % 8 != 0 || N < 1 || rank < 1 || rank > SPEAR_MAX_RANK) return SPEAR_ERR_INVALID_SHAPE;
+  if ((int64_t)K * 8 > INT32_MAX || (int64_t)N * 16 > INT32_MAX) return SPEAR_ERR_UNSUPPORTED;
   const EcInitLayout L = ec_init_layout(K, N, rank);
   if (!L.fits) return SPEAR_ERR_UNSUPPORTED;
   *bytes = L.bytes;

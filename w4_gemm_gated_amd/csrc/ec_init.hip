@@ -411,6 +411,8 @@ struct MmSplit {
   int slices, parts;
 };
 MmSplit mm_split(int64_t R, int64_t L, int64_t n) {
+  R = std::max<int64_t>(R, 1);
+  n = std::max<int64_t>(n, 1);
   const int64_t steps = std::max<int64_t>(1, ceil_div(L, kTile));
   const int64_t tiles = ceil_div(R, kTile) * ceil_div(n, kTile);
   const int64_t want = std::max<int64_t>(1, std::min({steps, kMaxParts, ceil_div(kTargetGroups, tiles)}));
@@ -428,6 +430,8 @@ EcInitLayout ec_init_layout(int64_t K, int64_t N, int64_t rank) {
   EcInitLayout L;
   L.l = (int)round_up(std::min<int64_t>(rank + kOversample, std::min(K, N)), 2);
   if (L.l > std::min(K, N)) L.l -= 2;
+  L.fits = L.l <= kMaxL && L.l >= rank && rank >= 1;
+  if (!L.fits) return L;
   const int64_t l = L.l;
   // partial sums of the largest split product
   const size_t part = std::max({mm_part_floats(K, N, l), mm_part_floats(N, K, l), mm_part_floats(l, K, l),
@@ -448,7 +452,6 @@ EcInitLayout ec_init_layout(int64_t K, int64_t N, int64_t rank) {
   L.Bt32 = take((size_t)N * rank * 4);
   L.sign = take((size_t)rank * 4);
   L.bytes = off;
-  L.fits = L.l <= kMaxL && L.l >= rank && rank >= 1;
   return L;
 }
 

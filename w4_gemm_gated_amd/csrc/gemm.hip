@@ -646,6 +646,12 @@ TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_
     t.split = 1;
     t.cps = (int)KC;
   }
+  // One launch's workgroup count (and the planner's sums over it) stays
+  // within 2^30.
+  if (ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16) * t.split > (int64_t)1 << 30) {
+    t.fits = false;
+    return t;
+  }
   t.mt = (int)ceil_div(M, t.tm);
   t.nt = (int)ceil_div(nblk, t.tn / 16);
   t.grid = t.mt * t.nt * t.split;

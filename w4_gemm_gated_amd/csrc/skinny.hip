@@ -991,7 +991,9 @@ SkinnyShape skinny_shape(int64_t M, int64_t K, int64_t N, int64_t rank, bool fus
   if (sh.S > 1) sh.ws_gemm_part = take(sizeof(float) * 4 * kWave * (size_t)sh.nbw * sh.T * sh.S);
   sh.ws_bytes = (sh.S > 1 || sh.P > 0) ? (off > kSyncHeaderBytes ? off : kSyncHeaderBytes) : 0;
   const size_t lds_room = kMaxLdsBytes - static_lds_bytes(sh.nbw);
-  sh.fits = kTiles + sh.T <= kMaxSyncWords && sh.lds <= lds_room && sh.lds_gemm <= lds_room &&
+  // best_score < 0: no split of K fits the kernel's chunks per wave (K above
+  // 64 splits x 32 chunks of 128).
+  sh.fits = best_score >= 0 && kTiles + sh.T <= kMaxSyncWords && sh.lds <= lds_room && sh.lds_gemm <= lds_room &&
             (size_t)sh.P * M * r1p * 8 <= kHandoffBytes;
   (void)M;
   return sh;
