@@ -217,6 +217,34 @@ def read_ceiling(torch, sp, nbytes, steps, graph):
     return best
 
 
+def mfma_ceiling(torch, sp):
+    """Practical ceiling of the matrix cores: back-to-back independent fp16
+    matrix instructions on register operands on every CU
+    (spear_debug_mfma_rate), right after the prefill timing (clocks settled).
+    Returns, per instruction, the best TFLOP/s over 1, 2 and 4 waves per SIMD
+    (median of three launches each)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(cus, dtype=torch.float32, device="cuda:0")
+    out = {}
+    for shape, name in ((0, "v_mfma_f32_16x16x32_f16"), (1, "v_mfma_f32_32x32x16_f16")):
+        best = None
+        for wps in (1, 2, 4):
+            iters = 20000 // wps
+            ts = []
+            for _ in range(3):
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                flops = sp.spear_debug_mfma_rate(shape, wps, iters, sink)
+                e.record()
+                torch.cuda.synchronize()
+                ts.append(s.elapsed_time(e) * 1e-3)
+            rate = flops / sorted(ts)[1] / 1e12
+            if best is None or rate > best[0]:
+                best = (rate, wps)
+        out[name] = {"TFLOP/s": round(best[0], 1), "waves_per_simd": best[1]}
+    return out
+
+
 PMC_COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_m16_hbm_traffic.json")
 
@@ -403,10 +431,13 @@ def main():
             ons.append(time_calls(torch, [on_call], args.prefill_steps, 3, graph))
             offs.append(time_calls(torch, [off_call], args.prefill_steps, 3, graph))
         t_on, t_off = sorted(ons)[1], sorted(offs)[1]
+        ceiling = mfma_ceiling(torch, sp)
         main_f, ec_f = workloads.algorithmic_flops(2048, wp["K"], wp["N"], wp["r"])
         tf = main_f / t_on / 1e12
+        c16 = ceiling["v_mfma_f32_16x16x32_f16"]["TFLOP/s"]
         prefill = {"us": round(t_on * 1e6, 2), "TFLOP/s": round(tf, 1),
                    "frac_mfma_fp16": round(tf / MFMA_FP16_PEAK_TFS, 4),
+                   "mfma_ceiling": ceiling, "frac_of_mfma_ceiling": round(tf / c16, 4),
                    "TFLOP/s_incl_ec": round((main_f + ec_f) / t_on / 1e12, 1),
                    "no_ec_us": round(t_off * 1e6, 2), "ec_overhead": round(t_on / t_off - 1.0, 4),
                    "variant": _binding_variant(pplans[(2048, "auto")])}

@@ -355,6 +355,22 @@ void spear_debug_fail_waits(int32_t on);
 spear_status_t spear_debug_stream_read(const void* src, size_t bytes, int32_t grid, void* sink, void* stream);
 
 /*
+ * spear_debug_mfma_rate -- the matrix cores' practical ceiling: one workgroup
+ * per CU of the current device, 4 x waves_per_simd waves each, every wave
+ * issuing `iterations` rounds of independent fp16 matrix instructions on
+ * register operands (shape 0: 8 accumulators of v_mfma_f32_16x16x32_f16, the
+ * instruction of this library's tile kernels; shape 1: 4 accumulators of
+ * v_mfma_f32_32x32x16_f16).  *flops (host) receives the launch's floating-point
+ * operations, so the caller's timing of it gives the rate.  sink: device
+ * memory of one float per CU (written only in a practically impossible case).
+ * A measurement aid, not part of the layer call.
+ * Errors: NULL_POINTER, INVALID_ARGUMENT (shape not 0/1, waves_per_simd not
+ *         1/2/4, iterations outside [1, 2^20]), MISALIGNED, HIP.
+ */
+spear_status_t spear_debug_mfma_rate(int32_t shape, int32_t waves_per_simd, int32_t iterations, void* sink,
+                                    void* stream, double* flops);
+
+/*
  * spear_ec_init -- data-free initialisation of the EC factors: A B = the
  * rank-r truncated SVD of the quantization residual E = W - dequant(Wq, s)
  * (SPEAR page, abstract: lightweight compensators of the quantization error;

@@ -253,6 +253,11 @@ void argument_checks() {
   char buf[64];
   CHECK(spear_take_error(buf, 1024, &code, nullptr) == SPEAR_ERR_WORKSPACE_TOO_SMALL, "take_error small");
   CHECK(spear_debug_stream_read(nullptr, 64, 1, buf, nullptr) == SPEAR_ERR_NULL_POINTER, "stream_read null");
+  double flops = 0.0;
+  CHECK(spear_debug_mfma_rate(0, 1, 10, nullptr, nullptr, &flops) == SPEAR_ERR_NULL_POINTER, "mfma_rate null");
+  CHECK(spear_debug_mfma_rate(2, 1, 10, buf, nullptr, &flops) == SPEAR_ERR_INVALID_ARGUMENT, "mfma_rate shape");
+  CHECK(spear_debug_mfma_rate(0, 1, 1 << 21, buf, nullptr, &flops) == SPEAR_ERR_INVALID_ARGUMENT,
+        "mfma_rate iterations");
   spear_debug_set_spin_limit(0);
   spear_debug_set_spin_limit(-1);
   spear_debug_fail_waits(1);

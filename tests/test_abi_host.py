@@ -59,6 +59,13 @@ def test_service_entry_points_check_arguments(lib):
     assert lib.spear_debug_stream_read(buf, 0, 1, buf, None) == 2
     assert lib.spear_debug_stream_read(buf, 24, 1, buf, None) == 2
     assert lib.spear_debug_stream_read(buf, 64, 0, buf, None) == 2
+    # spear_debug_mfma_rate: arguments, before any device query or launch
+    fl = ctypes.c_double(0.0)
+    assert lib.spear_debug_mfma_rate(0, 1, 10, None, None, ctypes.byref(fl)) == 1
+    assert lib.spear_debug_mfma_rate(0, 1, 10, buf, None, None) == 1
+    assert lib.spear_debug_mfma_rate(2, 1, 10, buf, None, ctypes.byref(fl)) == 8
+    assert lib.spear_debug_mfma_rate(0, 3, 10, buf, None, ctypes.byref(fl)) == 8
+    assert lib.spear_debug_mfma_rate(1, 4, 0, buf, None, ctypes.byref(fl)) == 8
     # the debug knobs take any value and return nothing
     lib.spear_debug_set_spin_limit(0)
     lib.spear_debug_set_spin_limit(-1)

@@ -111,6 +111,27 @@ def test_take_error_argument_checks():
     assert sp.spear_take_error(ws) == 0
 
 
+def test_mfma_rate_counts_and_runs():
+    """The matrix-rate aid reports the flops of its launch (instructions x
+    multiply-adds x 2 over every wave of one workgroup per CU) and the
+    measured rate lies below the published dense fp16 peak of 2.5 PF/s."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(cus, dtype=torch.float32, device=DEV)
+    for shape, per in ((0, 8 * 8192 * 2), (1, 4 * 16384 * 2)):
+        flops = sp.spear_debug_mfma_rate(shape, 2, 2000, sink)
+        assert flops == per * 2000 * 4 * 2 * cus
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        sp.spear_debug_mfma_rate(shape, 2, 2000, sink)
+        e.record()
+        torch.cuda.synchronize()
+        rate = flops / (s.elapsed_time(e) * 1e-3)
+        note(f"mfma shape {shape}: {rate / 1e12:.0f} TFLOP/s")
+        assert 2e14 < rate < 2.6e15
+    assert not sink.any()
+
+
 def test_stream_read_runs():
     src = torch.ones(1 << 20, dtype=torch.int32, device=DEV)
     sink = torch.zeros(512, dtype=torch.int32, device=DEV)

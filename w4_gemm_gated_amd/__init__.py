@@ -33,6 +33,7 @@ __all__ = [
     "spear_debug_set_spin_limit",
     "spear_debug_fail_waits",
     "spear_debug_stream_read",
+    "spear_debug_mfma_rate",
     "library",
     "SpearError",
 ]
@@ -340,3 +341,16 @@ def spear_debug_stream_read(src, grid, sink):
     st = library().spear_debug_stream_read(_ptr(src), src.numel() * src.element_size(), int(grid), _ptr(sink),
                                            _stream(src.device))
     _binding.check(st, "spear_debug_stream_read")
+
+
+def spear_debug_mfma_rate(shape, waves_per_simd, iterations, sink):
+    """Enqueue back-to-back matrix instructions on every CU (a measurement
+    aid); returns the launch's floating-point operations.  shape 0:
+    v_mfma_f32_16x16x32_f16, 1: v_mfma_f32_32x32x16_f16; sink: float32, one
+    per CU."""
+    _need(sink, "sink", torch.float32, 1)
+    flops = ctypes.c_double(0.0)
+    st = library().spear_debug_mfma_rate(int(shape), int(waves_per_simd), int(iterations), _ptr(sink),
+                                         _stream(sink.device), ctypes.byref(flops))
+    _binding.check(st, "spear_debug_mfma_rate")
+    return flops.value

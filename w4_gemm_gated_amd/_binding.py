@@ -48,6 +48,7 @@ EXPORTS = (
     "spear_debug_set_spin_limit",
     "spear_debug_fail_waits",
     "spear_debug_stream_read",
+    "spear_debug_mfma_rate",
 )
 
 
@@ -147,6 +148,8 @@ def load(path=None):
     lib.spear_debug_fail_waits.argtypes = [ctypes.c_int32]
     lib.spear_debug_stream_read.restype = ctypes.c_int
     lib.spear_debug_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.spear_debug_mfma_rate.restype = ctypes.c_int
+    lib.spear_debug_mfma_rate.argtypes = [i32, i32, i32, vp, vp, ctypes.POINTER(ctypes.c_double)]
     if path == LIB_PATH:
         _lib = lib
     return lib

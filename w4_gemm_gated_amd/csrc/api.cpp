@@ -326,4 +326,21 @@ spear_status_t spear_debug_stream_read(const void* src, size_t bytes, int32_t gr
   return hip_status(launch_stream_read(src, bytes, grid, sink, stream));
 }
 
+spear_status_t spear_debug_mfma_rate(int32_t shape, int32_t waves_per_simd, int32_t iterations, void* sink,
+                                    void* stream, double* flops) {
+  if (!sink || !flops) return SPEAR_ERR_NULL_POINTER;
+  if ((shape != 0 && shape != 1) || (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) ||
+      iterations < 1 || iterations > (1 << 20))
+    return SPEAR_ERR_INVALID_ARGUMENT;
+  if (!aligned(sink, 4)) return SPEAR_ERR_MISALIGNED;
+  int cus = 0;
+  const spear_status_t st = device_cus(&cus);
+  if (st != SPEAR_OK) return st;
+  // 16 x 16 x 32 and 32 x 32 x 16: 8192 and 16384 multiply-adds per
+  // instruction; 8 and 4 accumulators per wave and round.
+  const double per_round = shape == 0 ? 8.0 * 8192 * 2 : 4.0 * 16384 * 2;
+  *flops = per_round * iterations * 4.0 * waves_per_simd * cus;
+  return hip_status(launch_mfma_rate(shape, waves_per_simd, iterations, cus, sink, stream));
+}
+
 }  // extern "C"

@@ -193,6 +193,7 @@ hipError_t static_scratch(void** out, void* stream);
 hipError_t set_max_dynamic_lds(const void* kernel, int bytes);
 hipError_t launch_take_error(void* workspace, void* out, void* stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, int grid, void* sink, void* stream);
+hipError_t launch_mfma_rate(int shape, int waves_per_simd, int iterations, int grid, void* sink, void* stream);
 // Data-free EC initialisation (ec_init.hip): workspace layout (byte offsets)
 // and launch arguments.
 struct EcInitLayout {
