@@ -186,13 +186,13 @@ __global__ void ec_reduce_kernel(const float* __restrict__ part, int parts, int6
 __global__ void __launch_bounds__(kEiThreads) ec_cholinv_kernel(const float* __restrict__ G, int l, float* __restrict__ T) {
   extern __shared__ float sm[];
   float* a = sm;                        // [l][l]: G, then L in the lower triangle
-  float* x = sm + l * l;                // [l][l]: X = L^-1, column c owned by thread c
+  float* x = sm + l * l;                // [l][l]: the identity, then X = L^-1
   __shared__ float red[kEiThreads];
-  __shared__ int keep[kMaxL];
   const int tid = threadIdx.x;
   float dm = 0.0f;
   for (int e = tid; e < l * l; e += kEiThreads) {
     a[e] = G[e];
+    x[e] = (e / l == e % l) ? 1.0f : 0.0f;
     if (e / l == e % l) dm = fmaxf(dm, G[e]);
   }
   red[tid] = dm;
@@ -202,39 +202,32 @@ __global__ void __launch_bounds__(kEiThreads) ec_cholinv_kernel(const float* __r
     __syncthreads();
   }
   const float tol = 1e-12f * red[0];
+  // Column j of L and row j of X = L^-1 together (forward elimination on the
+  // identity): scale column j of L and row j of X by 1 / L[j][j], then take
+  // column j out of the trailing lower triangle and row j out of the later
+  // rows of X.  X[j][c] is nonzero only for c <= j.
   for (int j = 0; j < l; ++j) {
     const float d = a[j * l + j];
     const bool ok = d > tol && d > 0.0f;
-    const float piv = ok ? sqrtf(d) : 0.0f;
-    const float inv = ok ? 1.0f / piv : 0.0f;
-    // column j below the diagonal, then the trailing lower triangle
-    for (int i = j + 1 + tid; i < l; i += kEiThreads) a[i * l + j] *= inv;
-    __syncthreads();
-    const int m = l - j - 1;
-    for (int e = tid; e < m * m; e += kEiThreads) {
-      const int i = j + 1 + e / m, k = j + 1 + e % m;
-      if (k <= i) a[i * l + k] = fmaf(-a[i * l + j], a[k * l + j], a[i * l + k]);
-    }
-    if (tid == 0) {
-      a[j * l + j] = piv;
-      keep[j] = ok;
-    }
-    __syncthreads();
-  }
-  // X = L^-1 by forward substitution, one column per thread.
-  for (int c = tid; c < l; c += kEiThreads) {
-    for (int i = 0; i < l; ++i) {
-      float v = 0.0f;
-      if (i == c) v = keep[i] ? 1.0f / a[i * l + i] : 0.0f;
-      else if (i > c && keep[i]) {
-        float s = 0.0f;
-        for (int k = c; k < i; ++k) s = fmaf(a[i * l + k], x[k * l + c], s);
-        v = -s / a[i * l + i];
+    const float inv = ok ? rsqrtf(d) : 0.0f;
+    for (int e = tid; e < l + j + 1; e += kEiThreads) {
+      if (e < l) {
+        if (e > j) a[e * l + j] *= inv;
+      } else {
+        x[j * l + (e - l)] *= inv;
       }
-      x[i * l + c] = v;
     }
+    __syncthreads();
+    if (tid == 0) a[j * l + j] = ok ? d * inv : 0.0f;
+    const int m = l - j - 1;
+    for (int e = tid; e < m * l; e += kEiThreads) {
+      const int i = j + 1 + e / l, k = e % l;
+      const float lij = a[i * l + j];
+      if (k > j && k <= i) a[i * l + k] = fmaf(-lij, a[k * l + j], a[i * l + k]);
+      if (k <= j) x[i * l + k] = fmaf(-lij, x[j * l + k], x[i * l + k]);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // T = X^T
   for (int e = tid; e < l * l; e += kEiThreads) T[e] = x[(e % l) * l + e / l];
 }
@@ -265,8 +258,11 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int r, float* __restrict__ 
   }
   __syncthreads();
   auto pair = [&](int step, int k, int& p, int& q) {
-    if (k == 0) { p = step; q = m; }
-    else { p = (step + k) % m; q = (step - k + m) % m; }
+    if (k == 0) { p = step; q = m; return; }
+    p = step + k;
+    if (p >= m) p -= m;
+    q = step - k + m;
+    if (q >= m) q -= m;
   };
   for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
     // Off-diagonal and diagonal norms: stop when the off part is negligible.
@@ -291,7 +287,9 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int r, float* __restrict__ 
     }
     const float dia_all = red[0];
     __syncthreads();
-    if (!(off_all > 1e-14f * dia_all)) break;
+    // Converged when the off-diagonal part is below (1e-6)^2 of the diagonal
+    // (fp32 leaves about 1e-7 l of rounding there).
+    if (!(off_all > 1e-12f * dia_all)) break;
     for (int step = 0; step < m; ++step) {
       for (int k = tid; k < half; k += kEiThreads) {
         int p, q;
