@@ -371,6 +371,12 @@ def main():
     t_step = time_calls(torch, step_calls, args.steps, args.warmup, graph)
     step_bytes = sum(workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"]) for M in ms)
     value = step_bytes / t_step / 1e9
+    # Secondary figure, the other timing mode: eager launches from Python
+    # (each call's argument marshalling and launch on the host) when the
+    # headline is a graph replay, or the graph replay when it is eager.
+    t_other = time_calls(torch, step_calls, args.steps, args.warmup, not graph)
+    other = {"timing": "eager launches" if graph else "hip graph replay of back-to-back calls",
+             "ms_per_step": round(t_other * 1e3, 6), "GB/s": round(step_bytes / t_other / 1e9, 1)}
     per_m, overhead = {}, {}
     for M in ms:
         b = workloads.algorithmic_bytes(M, w["K"], w["N"], w["r"])
@@ -483,6 +489,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "timing": "hip graph replay of back-to-back calls" if graph else "eager launches",
+        "secondary_timing": other,
         "data": "synthetic",
         "config": {"workload": "decode q_proj 4096x4096, W4 per-channel + EC rank 32, gate bias -1, "
                                "1% outlier channels x20, M=1,4,16 per step, cold weights",
@@ -537,6 +544,15 @@ def mid_size(torch, sp, workloads, steps, graph):
                 r[f"{v}_us" + ("" if tau == 0.0 else f"_tau{tau:g}")] = round(
                     timed(lay, M, v, b_g, tau, plans[v], Ys, ws) * 1e6, 2)
         r["no_ec_us"] = round(timed(lay, M, "no_ec", 0.0, 0.0, plans["no_ec"], Ys, ws) * 1e6, 2)
+        # The skip threshold's departure from the exact definition, on the GPU:
+        # Y at tau = 0.05 against Y at tau = 0 (same inputs, first weight copy).
+        Wq, s, A, B, wg = lay.sets[0]
+        Ye = sp.spear_w4ec_linear(lay.X[:M], Wq, s, A, B, wg, b_g, 0.0, "auto", N=lay.N).float()
+        Yt = sp.spear_w4ec_linear(lay.X[:M], Wq, s, A, B, wg, b_g, 0.05, "auto", N=lay.N).float()
+        torch.cuda.synchronize()
+        rms = float(Ye.pow(2).mean().sqrt())
+        r["tau0.05_deviation"] = {"relL2": round(float((Yt - Ye).norm() / Ye.norm()), 7),
+                                  "maxabs_over_rms": round(float((Yt - Ye).abs().max()) / rms, 6)}
         best = min(r["fused_us"], r["split_us"])
         r["faster"] = "fused" if r["fused_us"] <= r["split_us"] else "split"
         r["ec_overhead"] = round(best / r["no_ec_us"] - 1.0, 4)
