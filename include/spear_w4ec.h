@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SPEAR_ABI_VERSION 2u
+#define SPEAR_ABI_VERSION 3u
 #define SPEAR_LAYOUT_ID 2u
 #define SPEAR_MAX_RANK 256
 #define SPEAR_GROUP_SIZE 128   /* the one group size of group-wise scales */
@@ -245,7 +245,7 @@ spear_status_t spear_schedule_ec_costs(const double* extra_us, const float* weig
  *            accumulation; must not alias any input.
  *   workspace  device memory of at least plan.workspace_bytes (16-byte
  *            aligned; may be NULL when that is 0).  It must be zero-filled
- *            before its first use.  Its first 256 KiB are a header owned by
+ *            before its first use.  Its first 1 MiB is a header owned by
  *            the library: cross-workgroup counters, which every call returns
  *            to zero, a call epoch, which every fused call advances by one,
  *            and the fused variants' ready flags and hand-off slabs, which
@@ -278,7 +278,7 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
  * library's own device array of SPEAR_NOALLOC_WORKSPACE_BYTES (32 MiB) per GPU,
  * kept until the process ends; its address is looked up on the first call on
  * each device, which also enqueues on `stream` a small kernel that zeroes the
- * array's 256 KiB header before the call.  Every call on one GPU shares that
+ * array's 1 MiB header before the call.  Every call on one GPU shares that
  * array: calls that overlap in time on one GPU race and must not be issued
  * (order them, e.g. on one stream).  Its sticky error word is read with
  * spear_take_error(NULL, 0, code_out, stream).
@@ -318,7 +318,7 @@ spear_status_t spear_ec_project(int32_t M, int32_t K, int32_t rank, const void* 
  * flag gave up.  Each set bit means at least one call on this workspace wrote
  * a wrong Y.  Ordered on `stream` like the calls it reports on.
  * workspace and workspace_bytes as passed to spear_w4ec_linear (at least the
- * 256 KiB header); workspace NULL with workspace_bytes 0 reads the word of
+ * 1 MiB header); workspace NULL with workspace_bytes 0 reads the word of
  * spear_w4ec_linear_noalloc's workspace on the current device.
  * Errors: NULL_POINTER, WORKSPACE_TOO_SMALL, MISALIGNED, HIP.
  */

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.spear_abi_version() == 2
+    assert lib.spear_abi_version() == 3
     for code, name in _binding.STATUS_NAMES.items():
         assert lib.spear_status_str(code).decode().startswith(name)
     assert lib.spear_status_str(99).decode() == "SPEAR_ERR_UNKNOWN"
@@ -164,7 +164,7 @@ def test_dispatch_rules(lib):
     assert st == 0 and p.variant == 3 and p.tile_m == 64 and p.split_k > 1 and p.workspace_bytes > 0
     st, p = plan(lib, 0, 512, 512, 16)
     assert st == 0
-    assert p.abi_version == 2 and p.layout_id == 2 and p.cus == 256
+    assert p.abi_version == 3 and p.layout_id == 2 and p.cus == 256
 
 
 def test_dispatch_is_deterministic(lib):

@@ -29,11 +29,13 @@ def cuda(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-# Three fused shapes: decode calls that take the producers' hand-off (one of
-# few rows on a K=8192 layer, one on a square 4096 layer), and a tiled call
-# whose EC workgroups raise ready flags.
+# Four fused shapes: decode calls that take the producers' hand-off (one of
+# few rows on a K=8192 layer, one on a square 4096 layer, one whose entries
+# fill most of the hand-off region), and a tiled call whose EC workgroups
+# raise ready flags.
 HANDOFF = (2, 8192, 1024, 64)
 HANDOFF_SQUARE = (2, 4096, 4096, 32)
+HANDOFF_LARGE = (16, 8192, 1024, 64)
 TILED = (130, 392, 200, 32)
 
 
@@ -59,7 +61,7 @@ def within(Y, Y_ref):
     return oracle.rel_l2(Y, Y_ref) <= 1e-3 and oracle.max_abs_over_rms(Y, Y_ref) <= 1e-2
 
 
-@pytest.mark.parametrize("shape,bit", [(HANDOFF, 1), (HANDOFF_SQUARE, 1), (TILED, 2)])
+@pytest.mark.parametrize("shape,bit", [(HANDOFF, 1), (HANDOFF_SQUARE, 1), (HANDOFF_LARGE, 1), (TILED, 2)])
 def test_wait_give_up_is_reported(shape, bit):
     note(f"forced give-up on fused shape {shape}")
     call, ws, Y_ref = fused_case(shape, seed=sum(shape))
@@ -82,7 +84,7 @@ def test_wait_give_up_is_reported(shape, bit):
     assert words[32 * 1024 // 4 + 32] == 0       # finisher count back at zero
 
 
-@pytest.mark.parametrize("shape", [HANDOFF, HANDOFF_SQUARE, TILED])
+@pytest.mark.parametrize("shape", [HANDOFF, HANDOFF_SQUARE, HANDOFF_LARGE, TILED])
 def test_epoch_wrap(shape):
     """The epoch word set to 2^32 - 2 (as after that many calls): the next call
     carries the largest tag, clears the header's tagged words and restarts the

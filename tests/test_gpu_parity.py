@@ -227,6 +227,21 @@ def test_fused_ragged_shapes(M, K, N, r):
     layer_case(X, W, A, B, w_g, -0.5, 0.0, "fused", f"fused ragged M={M} K={K} N={N} r={r}")
 
 
+@pytest.mark.parametrize("M,K,N,r", [(8, 14336, 4096, 64), (16, 14336, 4096, 64), (16, 8192, 1024, 64),
+                                     (13, 16384, 520, 64)])
+def test_fused_large_handoff(M, K, N, r):
+    """Decode calls whose producers' entries (P x M x (rank + 1) tagged values)
+    need most of the hand-off region: rank 64 on long K at 8-16 rows (up to
+    56-64 producers), every row of the output against the oracle."""
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=7 * M + K + N + r, outliers=True)
+    p = sp.spear_dispatch_plan(M, K, N, r, -0.5, variant="fused")
+    r1p = (r + 2) // 2 * 2
+    note(f"fused large hand-off M={M} K={K} N={N} r={r}: producers={p.producers} "
+         f"entries {p.producers * M * r1p * 8} B, split_k={p.split_k}")
+    assert p.ec_local == 0 and p.producers * M * r1p * 8 > 192 * 1024
+    layer_case(X, W, A, B, w_g, -0.5, 0.0, "fused", f"fused large hand-off M={M} K={K} N={N} r={r}")
+
+
 @pytest.mark.parametrize("M,K,N,r", [(3, 1000, 4096, 20), (7, 264, 4096, 36), (2, 520, 4096, 4),
                                      (5, 616, 6000, 52), (16, 512, 14336, 64), (4, 2048, 4096, 32)])
 def test_local_ec_ragged_shapes(M, K, N, r):

@@ -30,14 +30,15 @@ inline int64_t p_stride(int64_t rank) { return round_up(rank, 32); }
 // counters of the EC projection in [0, 32 KiB) and of the GEMM kernels in
 // [32 KiB, 64 KiB), which every call returns to zero (except the GEMM call
 // epoch, which every fused call advances), and the fused variant's hand-off
-// slabs in [64 KiB, 256 KiB), whose entries carry the epoch of the call that
-// wrote them.  All scratch lies after the header, so a zero-filled workspace
+// slabs in [64 KiB, 1 MiB), whose entries carry the epoch of the call that
+// wrote them (room for the producers' entries of rank 64 up to K = 16384 at
+// 16 rows).  All scratch lies after the header, so a zero-filled workspace
 // serves calls of any plan (each plan's counters and hand-off sit in the
 // header, never in another plan's scratch).
-constexpr size_t kSyncHeaderBytes = 256 * 1024;
+constexpr size_t kSyncHeaderBytes = 1024 * 1024;
 constexpr size_t kGemmSyncOffset = 32 * 1024;
 constexpr size_t kHandoffOffset = 64 * 1024;
-constexpr size_t kHandoffBytes = 192 * 1024;
+constexpr size_t kHandoffBytes = 960 * 1024;
 constexpr int64_t kMaxSyncWords = 8192;   // per counter region
 // Words of the GEMM counter region ([32 KiB, 64 KiB)), each hot one on its own
 // 128-byte line: fused finisher count, error flag, call epoch (advanced by

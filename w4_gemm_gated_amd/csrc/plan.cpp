@@ -42,28 +42,35 @@ spear_status_t check_desc(const spear_linear_desc_t& d) {
 // constants fitted to this library's kernels measured on MI355X (graph replay,
 // cold weights):
 //   t = launch + max(bytes / stream rate, main flops / matrix rate of the
-//       kernel family) + split-K exchange + the variant's EC cost.
-// Stream rate: a plain read of B bytes in one launch takes 1.65 us + B / 7.2
-// TB/s (8 MiB .. 256 MiB); the decode kernel streams at 4.64 TB/s after 2.6 us
-// (its EC-off calls of 8.4 and 29.4 MB).  Matrix rates: the 256-row tiles
-// reach 1.13 PF/s on the prefill shape, the 128- and 64-row tiles 0.87 and
-// 0.55 (mid-size M, K split), the decode kernel 0.26 (its M = 16 call over
-// M = 1).  EC cost: decode hand-off 3 us, 0.07 per producer and 0.08 per KiB
-// of a producer's A slab past 32 KiB; local EC 1.0 us plus every workgroup's
-// read of A from L2,
-// fused tiles 4 us plus the EC workgroups' read of X (1.3 TB/s, partly under
-// the GEMM), split variant one more launch plus its read of X and its flops.
+//       kernel family) + split-K exchange + the variant's EC cost,
+// and for the decode kernel also the X rows every column tile re-reads from
+// L2 (column tiles x M x K x 2 bytes).
+// Tiled kernels: a plain read of B bytes in one launch takes 1.65 us + B / 7.2
+// TB/s (8 MiB .. 256 MiB); matrix rates: the 256-row tiles reach 1.13 PF/s on
+// the prefill shape, the 128- and 64-row tiles 0.87 and 0.55 (mid-size M, K
+// split); EC cost of the fused tiles 4 us plus the EC workgroups' read of X
+// (1.3 TB/s, partly under the GEMM), of the split variant one more launch plus
+// its read of X and its flops.
+// Decode kernel (fitted to 120 calls: ten layer shapes, M = 1, 4, 8, 16, the
+// three variants; median error 4.5 %, largest 17 %): 2.46 us + bytes / 4.06
+// TB/s + X re-reads / 18.95 TB/s, 1.91 us for a K split; hand-off EC 2.04 us +
+// 0.063 per producer + 0.131 per thousand entries gathered (producers x rows
+// x (rank + 1)) + 0.018 per row; local EC 1.83 us plus every workgroup's read
+// of A from L2 (16.8 TB/s); split variant 7.11 us + 4.60 per MiB of A + 0.029
+// per row (its projection launch reads A with few workgroups).
 namespace {
 
 struct CostConstants {
-  double stream_bytes_per_us = 7.2e6, skinny_stream_bytes_per_us = 4.64e6;
-  double launch_skinny_us = 2.6, launch_tiled_us = 3.0;
+  double stream_bytes_per_us = 7.2e6, skinny_stream_bytes_per_us = 4.06e6, skinny_x_l2_bytes_per_us = 18.95e6;
+  double launch_skinny_us = 2.46, launch_tiled_us = 3.0;
   double mma_skinny = 0.26e9, mma_64 = 0.55e9, mma_128 = 0.87e9, mma_256 = 1.13e9;   // flop per us
-  double split_skinny_us = 2.0, split_tiled_us = 3.0;
-  double ec_handoff_us = 3.0, ec_handoff_per_producer_us = 0.07, ec_handoff_per_slab_kib_us = 0.08;
-  double ec_local_us = 1.0, l2_bytes_per_us = 30e6;
+  double split_skinny_us = 1.91, split_tiled_us = 3.0;
+  double ec_handoff_us = 2.04, ec_handoff_per_producer_us = 0.063, ec_handoff_per_kentry_us = 0.131,
+         ec_handoff_per_row_us = 0.018;
+  double ec_local_us = 1.83, l2_bytes_per_us = 16.8e6;
   double ec_fused_tiled_us = 4.0, ec_fused_x_bytes_per_us = 1.3e6;
   double ec_split_launch_us = 3.0, ec_split_x_bytes_per_us = 2.0e6, ec_split_flops_per_us = 0.5e9;
+  double ec_split_skinny_us = 7.11, ec_split_skinny_per_a_mib_us = 4.60, ec_split_skinny_per_row_us = 0.029;
 };
 
 double predict_call_us(const spear_plan_t& p) {
@@ -78,19 +85,25 @@ double predict_call_us(const spear_plan_t& p) {
   double t = (skinny ? c.launch_skinny_us : c.launch_tiled_us) +
              std::max(bytes / (skinny ? c.skinny_stream_bytes_per_us : c.stream_bytes_per_us),
                       2.0 * M * K * N / mma_rate);
+  // Decode: every column tile reads the X rows of its K range, all of X over
+  // the tile's splits.
+  if (skinny) t += std::ceil((double)n_pad(p.N) / p.tile_n) * M * K * 2.0 / c.skinny_x_l2_bytes_per_us;
   if (p.split_k > 1) t += skinny ? c.split_skinny_us : c.split_tiled_us;
   if (ec) {
     const double ec_flops = 2.0 * M * (K * (r + 1) + r * N);
-    if (p.variant == SPEAR_VARIANT_SPLIT) {
+    if (p.variant == SPEAR_VARIANT_SPLIT && skinny) {
+      t += c.ec_split_skinny_us + c.ec_split_skinny_per_a_mib_us * (2.0 * K * r / 1048576.0) +
+           c.ec_split_skinny_per_row_us * M;
+    } else if (p.variant == SPEAR_VARIANT_SPLIT) {
       t += c.ec_split_launch_us + 2.0 * M * K / c.ec_split_x_bytes_per_us + ec_flops / c.ec_split_flops_per_us;
     } else if (skinny && p.ec_local) {
       t += c.ec_local_us + 2.0 * K * r * (double)p.grid / c.l2_bytes_per_us;
     } else if (skinny) {
-      // The producers' chain: their count (the hand-off each consumer reads)
-      // and their A slab beyond 32 KiB (the slab each one streams).
-      const double slab_kib = std::ceil(K / std::max(1, p.producers)) * r * 2.0 / 1024.0;
-      t += c.ec_handoff_us + c.ec_handoff_per_producer_us * p.producers +
-           c.ec_handoff_per_slab_kib_us * std::max(0.0, slab_kib - 32.0);
+      // The producers' chain: their count, the entries every consumer gathers
+      // and the rows they carry.
+      const double entries = (double)p.producers * M * (double)round_up(p.rank + 1, 2);
+      t += c.ec_handoff_us + c.ec_handoff_per_producer_us * p.producers + c.ec_handoff_per_kentry_us * entries / 1000.0 +
+           c.ec_handoff_per_row_us * M;
     } else {
       t += c.ec_fused_tiled_us + 2.0 * M * K / c.ec_fused_x_bytes_per_us;
     }
