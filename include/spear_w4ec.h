@@ -193,7 +193,7 @@ spear_status_t spear_dispatch_plan(const spear_linear_desc_t* desc, spear_plan_t
  * the EC on, predicted_no_ec_us with it off) stays within slo_us, and the
  * total weight of the ECs kept on is the largest possible.  Exact 0/1
  * knapsack over the layers' extra time (EC on minus off), each rounded up to
- * a grid of at most 65536 steps of the slack (so rounding never breaks the
+ * a grid of the slack (as spear_schedule_ec_costs: rounding never breaks the
  * objective); among optimal sets the one that adds the least time.
  *   layers   host array [n_layers]; ec_on  host output [n_layers] (1: keep the
  *            EC; always 0 for rank 0); predicted_us host output (may be NULL):
@@ -213,8 +213,10 @@ spear_status_t spear_schedule_ec(const spear_sched_layer_t* layers, int32_t n_la
  * the caller gives: among the layers i with extra_us[i] >= 0 (a negative extra
  * marks a layer without an EC) and weight[i] > 0, the set of largest total
  * weight whose extra times, each rounded up to the grid unit
- * u = max(slack_us / 65536, 1e-9), sum to at most floor(slack_us / u) units;
- * ties go to the set of fewer units.  Weights are summed in layer order.
+ * u = max(slack_us / G, 1e-9), sum to at most min(G, floor(slack_us / u))
+ * units, with G = 65536 grid steps for up to 256 layers and
+ * max(256, floor(65536 x 256 / n)) beyond (so a call does about 2^24 cell
+ * updates and holds one bit per cell); ties go to the set of fewer units.  Weights are summed in layer order.
  * slack_us < 0: nothing is chosen.  ec_on host output [n]; added_us (may be
  * NULL): the chosen extra time.  Host only.
  * Errors: NULL_POINTER, INVALID_SHAPE (n outside [0, 4096]),

@@ -170,6 +170,19 @@ void scheduler(Rng& rng) {
     CHECK(on[n] == 7, "wrote past ec_on");
     if (slack >= 0.0) CHECK(sum <= slack * (1.0 + 1e-9) + 1e-6, "over the slack: %g > %g", sum, slack);
   }
+  {  // the largest instance: the coarse grid and the bit table at full size
+    const int n = 4096;
+    std::vector<double> extra(n);
+    std::vector<float> w(n);
+    for (int i = 0; i < n; ++i) {
+      extra[i] = rng.unit();
+      w[i] = (float)(0.1 + rng.unit());
+    }
+    std::vector<uint8_t> on(n + 1, 7);
+    double added = 0.0;
+    CHECK(spear_schedule_ec_costs(extra.data(), w.data(), n, 1000.0, on.data(), &added) == SPEAR_OK, "n = 4096");
+    CHECK(on[n] == 7 && added <= 1000.0 * (1.0 + 1e-9), "n = 4096 outputs");
+  }
   double e1[2] = {1.0, std::numeric_limits<double>::quiet_NaN()};
   float w1[2] = {1.0f, 1.0f};
   uint8_t on1[2];

@@ -93,6 +93,35 @@ def test_library_selection_matches_oracle():
 
 
 @needs_lib
+def test_library_selection_on_the_coarse_grid():
+    """Beyond 256 layers the grid coarsens with n; the library's choice is
+    still an optimum of that grid's knapsack (scipy's MILP on the same integer
+    costs), fits the slack, and 4096 layers take a fraction of a second."""
+    import time
+    from scipy.optimize import LinearConstraint, Bounds, milp
+    assert osch.grid_steps(256) == 65536 and osch.grid_steps(512) == 32768 and osch.grid_steps(4096) == 4096
+    rng = np.random.default_rng(23)
+    for n in (300, 600):
+        extra = rng.uniform(0.0, 2.0, n)
+        weights = rng.integers(1, 50, n).astype(np.float32)
+        slack = float(rng.uniform(50.0, 200.0))
+        on, added = sp.spear_schedule_ec_costs(list(extra), list(weights), slack)
+        unit, cap = osch.grid(slack, n)
+        units = np.array([osch.units_of(e, unit) for e in extra], dtype=float)
+        res = milp(c=-weights.astype(float), constraints=LinearConstraint(units[None, :], -np.inf, cap),
+                   integrality=np.ones(n), bounds=Bounds(0, 1))
+        assert res.status == 0
+        got = [i for i in range(n) if on[i]]
+        assert sum(units[i] for i in got) <= cap and added <= slack + 1e-9
+        assert abs(sum(float(weights[i]) for i in got) - (-res.fun)) < 1e-6, n
+    extra = list(rng.uniform(0.0, 1.0, 4096))
+    weights = list(rng.uniform(0.1, 1.0, 4096).astype(np.float32))
+    t0 = time.perf_counter()
+    on, added = sp.spear_schedule_ec_costs(extra, weights, 1000.0)
+    assert time.perf_counter() - t0 < 2.0 and added <= 1000.0 + 1e-9 and 0 < sum(on) < 4096
+
+
+@needs_lib
 def test_selection_argument_checks():
     with pytest.raises(sp.SpearError):
         sp.spear_schedule_ec_costs([1.0], [-1.0], 5.0)

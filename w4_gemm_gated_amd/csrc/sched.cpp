@@ -4,6 +4,7 @@
 // whose predicted batch latency (the planner's cost model) fits the SLO.
 // Pure host arithmetic on plans; nothing touches the device beyond the CU
 // count the planner may read.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -13,7 +14,12 @@
 namespace {
 
 constexpr int kMaxSchedLayers = 4096;
-constexpr int kSlackSteps = 65536;   // grid of the knapsack's capacity
+constexpr int kSlackSteps = 65536;   // grid of the knapsack's capacity, up to kFullGridLayers layers
+constexpr int kFullGridLayers = 256;
+
+// Grid steps for n layers: 65536 up to 256 layers, fewer beyond (65536 x 256
+// / n, at least 256), so a call stays near 2^24 cell updates.
+int slack_steps(int n) { return n <= kFullGridLayers ? kSlackSteps : std::max(256, kSlackSteps * kFullGridLayers / n); }
 
 }  // namespace
 
@@ -32,8 +38,9 @@ extern "C" spear_status_t spear_schedule_ec_costs(const double* extra_us, const 
   // true extra time never exceeds the slack).  best[c]: the largest weight
   // (summed in layer order) of a set of cost <= c, ties to the least cost;
   // layers with a negative extra (no EC) or no weight are never taken.
-  const double unit = std::max(slack_us / kSlackSteps, 1e-9);
-  const int cap = (int)std::min<double>(kSlackSteps, std::floor(slack_us / unit));
+  const int steps = slack_steps(n);
+  const double unit = std::max(slack_us / steps, 1e-9);
+  const int cap = (int)std::min<double>(steps, std::floor(slack_us / unit));
   std::vector<int> cost((size_t)n, 0);
   std::vector<int> items;
   for (int i = 0; i < n; ++i) {
@@ -45,7 +52,9 @@ extern "C" spear_status_t spear_schedule_ec_costs(const double* extra_us, const 
   }
   struct Cell { double w; int c; };
   std::vector<Cell> best((size_t)cap + 1, Cell{0.0, 0});
-  std::vector<std::vector<uint8_t>> take(items.size(), std::vector<uint8_t>((size_t)cap + 1, 0));
+  // take[t]: bit c set when item t improved best[c] (one bit per cell).
+  const size_t words = ((size_t)cap + 64) / 64;
+  std::vector<uint64_t> take(items.size() * words, 0);
   for (size_t t = 0; t < items.size(); ++t) {
     const int i = items[t], ci = cost[i];
     const double wi = weight[i];
@@ -54,14 +63,14 @@ extern "C" spear_status_t spear_schedule_ec_costs(const double* extra_us, const 
       const Cell cur = best[(size_t)c];
       if (cand.w > cur.w || (cand.w == cur.w && cand.c < cur.c)) {
         best[(size_t)c] = cand;
-        take[t][(size_t)c] = 1;
+        take[t * words + (size_t)c / 64] |= (uint64_t)1 << (c % 64);
       }
     }
   }
   double added = 0.0;
   int c = cap;
   for (size_t t = items.size(); t-- > 0;) {
-    if (take[t][(size_t)c]) {
+    if ((take[t * words + (size_t)c / 64] >> (c % 64)) & 1u) {
       const int i = items[t];
       ec_on[i] = 1;
       added += extra_us[i];
