@@ -280,7 +280,9 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
  * library's own device array of SPEAR_NOALLOC_WORKSPACE_BYTES (32 MiB) per GPU,
  * kept until the process ends; its address is looked up on the first call on
  * each device, which also enqueues on `stream` a small kernel that zeroes the
- * array's 1 MiB header before the call.  Every call on one GPU shares that
+ * array's 1 MiB header before the call.  That first call must not be made
+ * while `stream` is being captured into a graph (it returns SPEAR_ERR_HIP,
+ * with nothing enqueued); later calls may be captured.  Every call on one GPU shares that
  * array: calls that overlap in time on one GPU race and must not be issued
  * (order them, e.g. on one stream).  Its sticky error word is read with
  * spear_take_error(NULL, 0, code_out, stream).

@@ -69,3 +69,60 @@ def test_graph_replay_matches_eager(M, K, N, r, noalloc):
     else:
         assert sp.spear_take_error(ws) == 0
     del g
+
+
+FIRST_CALL_SCRIPT = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import workloads, w4_gemm_gated_amd as sp
+M, K, N, r = 4, 1024, 2048, 32
+X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=3, outliers=True)
+t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+Wq, s = sp.spear_pack_w4(t(W))
+args = (t(X), Wq, s, t(A), t(B), t(w_g), -0.5)
+plan = sp.spear_dispatch_plan(M, K, N, r, -0.5, 0.0, "fused")
+assert plan.workspace_bytes > 0
+Y = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+refused = False
+try:
+    with torch.cuda.graph(g):
+        sp.spear_w4ec_linear_noalloc(*args, N=N, plan=plan, Y=Y)
+except Exception as e:   # the library's refusal (ending an empty capture may raise on top of it)
+    refused = any("SPEAR_ERR_HIP" in str(x) for x in (e, e.__context__) if x is not None)
+assert refused, "the first call under capture was not refused"
+del g
+torch.cuda.synchronize()
+Y_eager = sp.spear_w4ec_linear_noalloc(*args, N=N, plan=plan).clone()
+Y_ws = sp.spear_w4ec_linear(*args, N=N, plan=plan)
+torch.cuda.synchronize()
+assert torch.equal(Y_eager, Y_ws)
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    sp.spear_w4ec_linear_noalloc(*args, N=N, plan=plan, Y=Y)
+for _ in range(3):
+    Y.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y_eager)
+print("first-call capture check passed", flush=True)
+"""
+
+
+def test_noalloc_first_call_under_capture_is_refused():
+    """In a fresh process (no earlier call has set up the library's array):
+    the first allocation-free call made under graph capture is refused with
+    nothing enqueued, the next eager call sets the array up and matches the
+    workspace entry point, and captured calls after it replay correctly."""
+    import os
+    import subprocess
+    import sys
+    repo = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    note("fresh process: first allocation-free call under capture")
+    res = subprocess.run([sys.executable, "-c", FIRST_CALL_SCRIPT, repo], capture_output=True, text=True,
+                         timeout=300)
+    out = res.stdout + res.stderr
+    assert res.returncode == 0, out[-4000:]
+    assert "first-call capture check passed" in out

@@ -7,9 +7,10 @@
 // is a stand-in, not a device address): at set-up, once per device with that
 // device current, hipGetSymbolAddress gives this device's address, which is
 // kept and used for every kernel argument.  Set-up also zeroes the array's
-// 256 KiB header with a fill kernel on the caller's stream, ordered before
+// workspace header with a fill kernel on the caller's stream, ordered before
 // the first call; every call returns the header's counters to zero, so later
-// calls need no clearing.  Every call on one GPU shares its array: calls that
+// calls need no clearing.  Set-up refuses a stream under graph capture: the
+// fill would be recorded into the graph instead of run.  Every call on one GPU shares its array: calls that
 // overlap on one GPU race (they must be ordered, e.g. on one stream).
 #include <atomic>
 #include <mutex>
@@ -47,6 +48,10 @@ hipError_t static_scratch(void** out, void* stream) {
   std::lock_guard<std::mutex> lock(g_setup_mu);
   p = g_scratch_ptr[dev].load(std::memory_order_acquire);
   if (!p) {
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing((hipStream_t)stream, &capture);
+    if (e != hipSuccess) return e;
+    if (capture != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
