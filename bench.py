@@ -256,15 +256,28 @@ DECODE_SOURCES = ("w4_gemm_gated_amd/csrc/skinny.hip", "w4_gemm_gated_amd/csrc/d
                   "include/spear_w4ec.h")
 
 
-def source_digest():
-    """Digest of the decode kernel's sources, to tell whether stored counter
-    readings still describe the library as built."""
+def _code_only(text):
+    """Source text without C/C++ comments and blank-line differences (what
+    the compiler sees), so edits to comments do not change the digest."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def source_digest(read=None):
+    """Digest of the decode kernel's sources (code only), to tell whether
+    stored counter readings still describe the library as built.  read(name)
+    returns a file's text (default: the working tree)."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
+    if read is None:
+        def read(name):
+            with open(os.path.join(root, name), encoding="utf-8") as f:
+                return f.read()
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
-        with open(os.path.join(root, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        h.update(name.encode() + b"\0" + _code_only(read(name)).encode())
     return h.hexdigest()[:16]
 
 
