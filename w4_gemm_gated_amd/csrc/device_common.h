@@ -35,7 +35,11 @@ __device__ __forceinline__ float4_t mfma16x16x32(const half8_t& a, const half8_t
 // Decode one packed word (eight 4-bit codes u, fields in k order
 // 0,2,4,6,1,3,5,7) into the eight fp16 values q = u - 8 in k order.
 // OR-ing 0x6400 into a 16-bit half holding u (< 16) in its low mantissa bits
-// gives exactly the fp16 value 1024 + u; subtracting 1032 leaves u - 8.
+// gives exactly the fp16 value 1024 + u; subtracting 1032 leaves u - 8.  A
+// code in mantissa bits 4..7 gives 1024 + 16 u instead, and one fused
+// multiply-add (x / 16 - 72) leaves u - 8, exactly (64 + u is an fp16
+// integer).  So the word and one copy shifted by 8 cover all eight codes:
+// one shift, four AND-ORs, two packed subtractions and two packed FMAs.
 // (x & m) | e in one instruction (the compiler emits an AND and an OR).
 // One scalar operand at most (one constant-bus read per instruction).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) {
@@ -44,16 +48,19 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t e) {
   return d;
 }
 __device__ __forceinline__ half8_t decode_w4(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, e = 0x64006400u;
-  const uint32_t d0 = and_or(w, m, e);
-  const uint32_t d1 = and_or(w >> 4, m, e);
-  const uint32_t d2 = and_or(w >> 8, m, e);
-  const uint32_t d3 = and_or(w >> 12, m, e);
+  const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, e = 0x64006400u;
+  const uint32_t w8 = w >> 8;
+  const uint32_t d0 = and_or(w, lo, e);     // fields 0, 4 -> 1024 + u
+  const uint32_t d1 = and_or(w, hi, e);     // fields 1, 5 -> 1024 + 16 u
+  const uint32_t d2 = and_or(w8, lo, e);    // fields 2, 6 -> 1024 + u
+  const uint32_t d3 = and_or(w8, hi, e);    // fields 3, 7 -> 1024 + 16 u
   const half2_t bias = {(half_t)1032.0f, (half_t)1032.0f};
+  const half2_t sixteenth = {(half_t)0.0625f, (half_t)0.0625f};
+  const half2_t bias16 = {(half_t)-72.0f, (half_t)-72.0f};
   const half2_t h0 = __builtin_bit_cast(half2_t, d0) - bias;
-  const half2_t h1 = __builtin_bit_cast(half2_t, d1) - bias;
+  const half2_t h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, d1), sixteenth, bias16);
   const half2_t h2 = __builtin_bit_cast(half2_t, d2) - bias;
-  const half2_t h3 = __builtin_bit_cast(half2_t, d3) - bias;
+  const half2_t h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, d3), sixteenth, bias16);
   half8_t r;
   r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
   r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];

@@ -237,15 +237,35 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   // (slot ^ (row % 16)).
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
   const uint32_t row_bytes = (uint32_t)a.K * 2u;
-  auto issue_x = [&](int kc, int st) {
+  // A step whose 128 k lie inside K takes the unit's offset at k = 0, the
+  // same every step, and adds the step's k as the scalar offset; only a last
+  // step past K computes per-unit offsets (units at k >= K sent outside).
+  uint32_t xoff[kCopiesPerWave];
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) {
-      const int row = (w * kCopiesPerWave + i) * 4 + lane / 16;
-      const int unit = (lane % 16) ^ (row % 16);
-      const int k = kc * kKt + unit * 8;
-      const uint32_t voff = k < a.K ? (uint32_t)(m0 + row) * row_bytes + (uint32_t)k * 2u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (lds_void_t*)(xs + (size_t)st * kStageHalves + (size_t)(row - lane / 16) * kKt), 16, voff, 0, 0, 0);
+  for (int i = 0; i < kCopiesPerWave; ++i) {
+    const int row = (w * kCopiesPerWave + i) * 4 + lane / 16;
+    xoff[i] = (uint32_t)(m0 + row) * row_bytes + (uint32_t)((lane % 16) ^ (row % 16)) * 16u;
+  }
+  const uint32_t* xo = xoff;
+  auto issue_x = [&](int kc, int st) {
+    if ((kc + 1) * kKt <= a.K) {
+#pragma unroll
+      for (int i = 0; i < kCopiesPerWave; ++i) {
+        const int row = (w * kCopiesPerWave + i) * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (lds_void_t*)(xs + (size_t)st * kStageHalves + (size_t)row * kKt), 16, xo[i],
+            (uint32_t)kc * (kKt * 2u), 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kCopiesPerWave; ++i) {
+        const int row = (w * kCopiesPerWave + i) * 4 + lane / 16;
+        const int unit = (lane % 16) ^ (row % 16);
+        const int k = kc * kKt + unit * 8;
+        const uint32_t voff = k < a.K ? (uint32_t)(m0 + row) * row_bytes + (uint32_t)k * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (lds_void_t*)(xs + (size_t)st * kStageHalves + (size_t)(row - lane / 16) * kKt), 16, voff, 0, 0, 0);
+      }
     }
   };
   // Packed weights through a buffer resource (panels >= NBLK clamped: their
