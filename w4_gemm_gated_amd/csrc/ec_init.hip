@@ -22,8 +22,8 @@
 // Products (E V, E^T Y, Gram matrices, basis changes) share one tiled fp32
 // kernel, K-split where its tiles alone would not fill the CUs.  The Cholesky
 // factor and the eigen-decomposition of the l x l Gram matrices run on one
-// workgroup each, in LDS (l <= 128): Cholesky by columns, the eigenpairs by
-// parallel cyclic Jacobi.
+// workgroup each (l <= 128): Cholesky by columns with the triangle in
+// registers, the eigenpairs by parallel cyclic Jacobi in LDS.
 #include <algorithm>
 #include <cmath>
 
@@ -176,24 +176,49 @@ __global__ void ec_reduce_kernel(const float* __restrict__ part, int parts, int6
 
 // -------------------------------------------------------------- Cholesky QR
 // T = L^-T from the Cholesky factor of the Gram matrix G = Y^T Y = L L^T
-// (l x l, one workgroup, in LDS), so that Y T has orthonormal columns: one
+// (l x l, one workgroup), so that Y T has orthonormal columns: one
 // pass of Cholesky QR (applied twice, it is CholeskyQR2: Fukaya, Nakatsukasa,
 // Yanagisawa and Yamamoto, "CholeskyQR2: a simple and communication-avoiding
 // algorithm for computing a tall-skinny QR factorization", 2014).  A column
 // whose pivot is not above 1e-12 of the largest diagonal entry (a direction
 // the block does not span: a zero or rank-deficient residual) is dropped: its
 // column of L is zeroed and its column of T is zero.
+// Thread t owns the lower-triangle positions e = t, t + 256, ... (row i,
+// column k, e = i (i + 1) / 2 + k) of both L (from G) and X = L^-1 (from the
+// identity) in registers; only the current column of L and row of X pass
+// through LDS.  Column j: the owner of (j, j) publishes the pivot; the owners
+// of column j of L and of row j of X scale them by its inverse square root
+// and publish them; every thread then takes column j out of its trailing
+// positions of L (k > j) and row j out of its positions of X below it
+// (i > j, k <= j).
+// kCholElems positions per thread cover l (l + 1) / 2 <= 256 kCholElems; the
+// launch takes the smallest instance that covers l.
+constexpr int chol_elems(int l) { return (l * (l + 1) / 2 + kEiThreads - 1) / kEiThreads; }
+
+template <int kCholElems>
 __global__ void __launch_bounds__(kEiThreads) ec_cholinv_kernel(const float* __restrict__ G, int l, float* __restrict__ T) {
-  extern __shared__ float sm[];
-  float* a = sm;                        // [l][l]: G, then L in the lower triangle
-  float* x = sm + l * l;                // [l][l]: the identity, then X = L^-1
+  // col[0, kMaxL): column j of L; col[kMaxL, 2 kMaxL): row j of X.
+  __shared__ float col[2 * kMaxL];
   __shared__ float red[kEiThreads];
+  __shared__ float piv;
+  static_assert(kMaxL == 128, "row and column indexes in 8 bits, i & 127 in range");
   const int tid = threadIdx.x;
+  const int count = l * (l + 1) / 2;
+  float a[kCholElems], x[kCholElems];
+  int ik[kCholElems];    // (i << 8) | k; -1 past the triangle (row -1: never below, column 255: never j)
   float dm = 0.0f;
-  for (int e = tid; e < l * l; e += kEiThreads) {
-    a[e] = G[e];
-    x[e] = (e / l == e % l) ? 1.0f : 0.0f;
-    if (e / l == e % l) dm = fmaxf(dm, G[e]);
+#pragma unroll
+  for (int u = 0; u < kCholElems; ++u) {
+    const int e = tid + u * kEiThreads;
+    int i = (int)((sqrtf(8.0f * (float)e + 1.0f) - 1.0f) * 0.5f);
+    while (i * (i + 1) / 2 > e) --i;
+    while ((i + 1) * (i + 2) / 2 <= e) ++i;
+    const int k = e - i * (i + 1) / 2;
+    const bool valid = e < count;
+    ik[u] = valid ? (i << 8) | k : -1;
+    a[u] = valid ? G[i * l + k] : 0.0f;
+    x[u] = (valid && i == k) ? 1.0f : 0.0f;
+    if (valid && i == k) dm = fmaxf(dm, a[u]);
   }
   red[tid] = dm;
   __syncthreads();
@@ -202,41 +227,64 @@ __global__ void __launch_bounds__(kEiThreads) ec_cholinv_kernel(const float* __r
     __syncthreads();
   }
   const float tol = 1e-12f * red[0];
-  // Column j of L and row j of X = L^-1 together (forward elimination on the
-  // identity): scale column j of L and row j of X by 1 / L[j][j], then take
-  // column j out of the trailing lower triangle and row j out of the later
-  // rows of X.  X[j][c] is nonzero only for c <= j.
   for (int j = 0; j < l; ++j) {
-    const float d = a[j * l + j];
+    const int jj = (j << 8) | j;
+#pragma unroll
+    for (int u = 0; u < kCholElems; ++u)
+      if (ik[u] == jj) piv = a[u];
+    __syncthreads();
+    const float d = piv;
     const bool ok = d > tol && d > 0.0f;
     const float inv = ok ? rsqrtf(d) : 0.0f;
-    for (int e = tid; e < l + j + 1; e += kEiThreads) {
-      if (e < l) {
-        if (e > j) a[e * l + j] *= inv;
-      } else {
-        x[j * l + (e - l)] *= inv;
+    // Publish column j of L (its diagonal: sqrt(d), or 0 when dropped) and
+    // row j of X, scaled; masked stores, no loads.
+#pragma unroll
+    for (int u = 0; u < kCholElems; ++u) {
+      const int i = ik[u] >> 8, k = ik[u] & 255;
+      if (k == j) {
+        a[u] = i == j ? (ok ? d * inv : 0.0f) : a[u] * inv;
+        col[i] = a[u];
+      }
+      if (i == j) {
+        x[u] *= inv;
+        col[kMaxL + k] = x[u];
       }
     }
     __syncthreads();
-    if (tid == 0) a[j * l + j] = ok ? d * inv : 0.0f;
-    const int m = l - j - 1;
-    for (int e = tid; e < m * l; e += kEiThreads) {
-      const int i = j + 1 + e / l, k = e % l;
-      const float lij = a[i * l + j];
-      if (k > j && k <= i) a[i * l + k] = fmaf(-lij, a[k * l + j], a[i * l + k]);
-      if (k <= j) x[i * l + k] = fmaf(-lij, x[j * l + k], x[i * l + k]);
+    // Trailing update, branch-free so that all the loads issue together:
+    // L positions (i > j, k > j) take L[i][j] L[k][j] off, X positions
+    // (i > j, k <= j) take L[i][j] X[j][k] off; the others get a zero factor
+    // (every slot a position above row j reads was written this column).
+    float li[kCholElems], ck[kCholElems];
+#pragma unroll
+    for (int u = 0; u < kCholElems; ++u) {
+      const int i = ik[u] >> 8, k = ik[u] & 255;
+      li[u] = col[i & (kMaxL - 1)];
+      ck[u] = col[k > j ? k : kMaxL + k];
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kCholElems; ++u) {
+      const int i = ik[u] >> 8, k = ik[u] & 255;
+      const float fa = i > j && k > j ? li[u] : 0.0f;
+      const float fx = i > j && k <= j ? li[u] : 0.0f;
+      a[u] = fmaf(-fa, ck[u], a[u]);
+      x[u] = fmaf(-fx, ck[u], x[u]);
+    }
   }
-  // T = X^T
-  for (int e = tid; e < l * l; e += kEiThreads) T[e] = x[(e % l) * l + e / l];
+  // T = X^T: zeros where X is zero (above its diagonal), the owned values elsewhere.
+  for (int e = tid; e < l * l; e += kEiThreads)
+    if (e % l < e / l) T[e] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kCholElems; ++u)
+    if (ik[u] >= 0) T[(ik[u] & 255) * l + (ik[u] >> 8)] = x[u];
 }
 
 // -------------------------------------------------------------- Jacobi
 // Rayleigh-Ritz step: eigen-decomposition of the symmetric G [l][l] (l even,
 // <= 128) by cyclic Jacobi, with the l/2 rotations of a step on disjoint
 // row/column pairs (the round-robin "circle" schedule: index l - 1 fixed,
-// the others rotating, so l - 1 steps pair every two indexes once).  Outputs,
+// the others rotating, so l - 1 steps pair every two indexes once; a step
+// rotates every 2 x 2 block of a on both sides in one pass).  Outputs,
 // eigenpairs ordered by decreasing eigenvalue L_j = s_j^2:
 //   TA = W_r diag(L_r^-1/4) [l][r]   (A = Y TA)
 //   TB = W_r diag(L_r^+1/4) [l][r]   (B^T = V TB)
@@ -251,6 +299,7 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int r, float* __restrict__ 
   float* cs = v + l * l;                // [l/2][2] rotation c, s
   int* ord = reinterpret_cast<int*>(cs + l);     // [l] eigenpair order
   __shared__ float red[kEiThreads];
+  __shared__ int pq[kMaxL];             // the step's pairs (p, q)
   const int tid = threadIdx.x, half = l / 2, m = l - 1;
   for (int e = tid; e < l * l; e += kEiThreads) {
     a[e] = G[e];
@@ -304,31 +353,38 @@ ec_jacobi_kernel(const float* __restrict__ G, int l, int r, float* __restrict__ 
         }
         cs[2 * k] = c;
         cs[2 * k + 1] = s;
+        pq[2 * k] = p;
+        pq[2 * k + 1] = q;
       }
       __syncthreads();
-      // columns p, q of a and v:  (x_p, x_q) <- (c x_p - s x_q, s x_p + c x_q)
-      for (int e = tid; e < half * l; e += kEiThreads) {
-        const int k = e / l, i = e % l;
-        int p, q;
-        pair(step, k, p, q);
-        const float c = cs[2 * k], s = cs[2 * k + 1];
-        const float xp = a[i * l + p], xq = a[i * l + q];
-        a[i * l + p] = c * xp - s * xq;
-        a[i * l + q] = s * xp + c * xq;
-        const float vp = v[i * l + p], vq = v[i * l + q];
-        v[i * l + p] = c * vp - s * vq;
-        v[i * l + q] = s * vp + c * vq;
+      // Every 2 x 2 block (rows p1, q1 of pair k1, columns p2, q2 of pair
+      // k2) in one pass: columns (x_p, x_q) <- (c x_p - s x_q, s x_p + c x_q)
+      // with pair k2's rotation, then rows the same way with pair k1's; the
+      // pairs are disjoint, so the blocks are too.  Then the columns of v.
+      const int tx = tid % 16, ty = tid / 16;
+      for (int k1 = ty; k1 < half; k1 += 16) {
+        const int p1 = pq[2 * k1], q1 = pq[2 * k1 + 1];
+        const float c1 = cs[2 * k1], s1 = cs[2 * k1 + 1];
+        for (int k2 = tx; k2 < half; k2 += 16) {
+          const int p2 = pq[2 * k2], q2 = pq[2 * k2 + 1];
+          const float c2 = cs[2 * k2], s2 = cs[2 * k2 + 1];
+          const float xpp = a[p1 * l + p2], xpq = a[p1 * l + q2], xqp = a[q1 * l + p2], xqq = a[q1 * l + q2];
+          const float ypp = c2 * xpp - s2 * xpq, ypq = s2 * xpp + c2 * xpq;   // row p1, columns rotated
+          const float yqp = c2 * xqp - s2 * xqq, yqq = s2 * xqp + c2 * xqq;   // row q1
+          a[p1 * l + p2] = c1 * ypp - s1 * yqp;
+          a[q1 * l + p2] = s1 * ypp + c1 * yqp;
+          a[p1 * l + q2] = c1 * ypq - s1 * yqq;
+          a[q1 * l + q2] = s1 * ypq + c1 * yqq;
+        }
       }
-      __syncthreads();
-      // rows p, q of a
-      for (int e = tid; e < half * l; e += kEiThreads) {
-        const int k = e / l, j = e % l;
-        int p, q;
-        pair(step, k, p, q);
-        const float c = cs[2 * k], s = cs[2 * k + 1];
-        const float xp = a[p * l + j], xq = a[q * l + j];
-        a[p * l + j] = c * xp - s * xq;
-        a[q * l + j] = s * xp + c * xq;
+      for (int i = ty; i < l; i += 16) {
+        for (int k2 = tx; k2 < half; k2 += 16) {
+          const int p2 = pq[2 * k2], q2 = pq[2 * k2 + 1];
+          const float c2 = cs[2 * k2], s2 = cs[2 * k2 + 1];
+          const float vp = v[i * l + p2], vq = v[i * l + q2];
+          v[i * l + p2] = c2 * vp - s2 * vq;
+          v[i * l + q2] = s2 * vp + c2 * vq;
+        }
       }
       __syncthreads();
     }
@@ -422,6 +478,24 @@ size_t mm_part_floats(int64_t R, int64_t L, int64_t n) {
   return p.parts > 1 ? (size_t)p.parts * R * n : 0;
 }
 
+// The Cholesky-inverse instance whose positions per thread cover l (l is at
+// most kMaxL).
+void launch_cholinv(const float* G, int l, float* T, hipStream_t s) {
+  const dim3 one(1), threads(kEiThreads);
+  if (l <= 32)
+    hipLaunchKernelGGL(ec_cholinv_kernel<chol_elems(32)>, one, threads, 0, s, G, l, T);
+  else if (l <= 48)
+    hipLaunchKernelGGL(ec_cholinv_kernel<chol_elems(48)>, one, threads, 0, s, G, l, T);
+  else if (l <= 64)
+    hipLaunchKernelGGL(ec_cholinv_kernel<chol_elems(64)>, one, threads, 0, s, G, l, T);
+  else if (l <= 80)
+    hipLaunchKernelGGL(ec_cholinv_kernel<chol_elems(80)>, one, threads, 0, s, G, l, T);
+  else if (l <= 96)
+    hipLaunchKernelGGL(ec_cholinv_kernel<chol_elems(96)>, one, threads, 0, s, G, l, T);
+  else
+    hipLaunchKernelGGL(ec_cholinv_kernel<chol_elems(kMaxL)>, one, threads, 0, s, G, l, T);
+}
+
 }  // namespace
 
 EcInitLayout ec_init_layout(int64_t K, int64_t N, int64_t rank) {
@@ -470,10 +544,8 @@ hipError_t launch_ec_init(const EcInitArgs& a, void* stream) {
   float* sign = (float*)(ws + L.sign);
   const int K = a.K, N = a.N, l = L.l, r = a.rank;
   const int KC = (int)(k_pad(K) / kKChunk), NP = (int)n_pad(N);
-  const size_t chol_lds = (size_t)2 * l * l * 4;
   const size_t jacobi_lds = (size_t)2 * l * l * 4 + (size_t)2 * l * 4;
   hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ec_jacobi_kernel), (int)jacobi_lds);
-  if (e == hipSuccess) e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ec_cholinv_kernel), (int)chol_lds);
   if (e != hipSuccess) return e;
   // C[R][n] = op(E) D, K-split into the partial-sum buffer where that fills the CUs.
   auto mm = [&](bool trans, const float* Ein, const float* D, float* C, int R, int Lin, int n) {
@@ -502,7 +574,7 @@ hipError_t launch_ec_init(const EcInitArgs& a, void* stream) {
       const float* src = pass == 0 ? X : Y2;
       float* dst = pass == 0 ? Y2 : X;
       mm(true, src, src, G, l, R, l);
-      hipLaunchKernelGGL(ec_cholinv_kernel, dim3(1), dim3(kEiThreads), chol_lds, s, G, l, T);
+      launch_cholinv(G, l, T, s);
       mm(false, src, T, dst, R, l, l);
     }
   };
