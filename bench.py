@@ -55,7 +55,7 @@ def parse():
                     help="for hardware-counter runs: a few eager decode calls (M=16), one plain device copy "
                          "of 256 MiB and one streaming read of 64 MiB (the counters' calibrations), no timing line")
     ap.add_argument("--pmc-prefill", action="store_true",
-                    help="for hardware-counter runs: a few eager prefill calls (fused, then EC off), no timing line")
+                    help="for hardware-counter runs: a few eager prefill calls (AUTO variant, then EC off), no timing line")
     return ap.parse_args()
 
 
@@ -296,8 +296,8 @@ def stored_traffic():
 
 
 def pmc_prefill(torch, sp, workloads):
-    """Eager prefill calls for rocprofv3 --pmc runs: 6 fused, then 6 with the
-    EC off (each dispatch reported apart)."""
+    """Eager prefill calls for rocprofv3 --pmc runs: 6 of the AUTO variant,
+    then 6 with the EC off (each dispatch reported apart)."""
     wp = workloads.workload(3)
     pre = Layer(torch, sp, wp, 2)
     Ys = [torch.empty((2048, wp["N"]), dtype=torch.float16, device="cuda:0")]

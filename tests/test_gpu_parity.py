@@ -271,11 +271,12 @@ def test_tiled_ragged_shapes(M, K, N, r, variant):
 
 
 @pytest.mark.parametrize("variant", ["fused", "split", "no_ec"])
-@pytest.mark.parametrize("M,K,N,r", [(2100, 1000, 7000, 36), (1500, 520, 7168, 64)])
+@pytest.mark.parametrize("M,K,N,r", [(2100, 1000, 7000, 36), (3100, 264, 3360, 36), (1500, 520, 7168, 64),
+                                     (1000, 200, 10750, 64)])
 def test_large_tile_ragged_shapes(M, K, N, r, variant):
-    """The 256-row tiles (256 x 256 and 256 x 224) on a partial last row
-    tile, a K tail, a partial last column tile and a partial 32-column group;
-    every element of Y."""
+    """The large tiles (256 x 256, 256 x 224 and 128 x 448, the last in
+    plain and XCD tile order) on a partial last row tile, a K tail, a partial
+    last column tile and a partial 32-column group; every element of Y."""
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=7 * M + K + N + r, outliers=True)
     if variant == "no_ec":
         A = B = w_g = None

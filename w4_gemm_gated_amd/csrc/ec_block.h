@@ -201,8 +201,8 @@ __device__ __forceinline__ void ec_block(const EcKArgs& a, unsigned char* lds, i
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(a.A, (uint32_t)((size_t)a.K * a.rank * 2));
   // A sub-slab s.  DMA layout: the rows are copied verbatim, 16 bytes per
   // unit; a thread loads its units (at most kAUnits: SS * rank / 8 <= 2048)
-  // into registers while the current stage is in use and writes them to the
-  // other stage after it (units past the sub-slab read as zeros).  A copy
+  // into registers a sub-slab ahead and writes them to the stage the matrix
+  // work no longer reads (units past the sub-slab read as zeros).  A copy
   // straight to LDS would make the compiler hold the transposing LDS reads of
   // the current stage until the copies of the next had landed.
   constexpr int kAUnits = 8;
@@ -260,24 +260,24 @@ __device__ __forceinline__ void ec_block(const EcKArgs& a, unsigned char* lds, i
   float4_t acc[PB + 1];                        // the gate logit in acc[PB]
 #pragma unroll
   for (int j = 0; j <= PB; ++j) acc[j] = zero_float4();
+  // Loads run one sub-slab ahead of the matrix work and are issued before
+  // anything waits: the first two sub-slabs' A, X and gate loads go out
+  // together (one memory round trip), and sub-slab s + 2's when s + 1's A
+  // reaches the LDS.
   half8_t xcur[KB], xnext[KB], gcur[KB], gnext[KB];
-  u32x4_t areg[kAUnits];
-  if (DMA) {
-    load_A(0, areg);
-    store_A(0, areg);
-  } else {
-    fill_A(0, 0);
-  }
+  u32x4_t a0[kAUnits], a1[kAUnits];
+  if (DMA) load_A(0, a0);
+  else fill_A(0, 0);
   load_x(0, xcur, gcur);
+  if (nsub > 1) {
+    if (DMA) load_A(1, a1);
+    load_x(1, xnext, gnext);
+  }
+  if (DMA) store_A(0, a0);
   for (int s = 0; s < nsub; ++s) {
     const int st = s & 1;
-    wait_vm_all();                              // this sub-slab's X and gate fragments
     __syncthreads();                            // stage st complete; stage st^1 free
-    if (s + 1 < nsub) {
-      if (DMA) load_A(s + 1, areg);
-      else fill_A(s + 1, st ^ 1);
-      load_x(s + 1, xnext, gnext);
-    }
+    if (!DMA && s + 1 < nsub) fill_A(s + 1, st ^ 1);
     const half_t* As = stage_A(st);
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
@@ -290,11 +290,15 @@ __device__ __forceinline__ void ec_block(const EcKArgs& a, unsigned char* lds, i
       acc[PB] = mfma16x16x32(xcur[i], gcur[i], acc[PB]);
     }
     if (s + 1 < nsub) {
-      if (DMA) store_A(st ^ 1, areg);
+      if (DMA) store_A(st ^ 1, a1);
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
         xcur[i] = xnext[i];
         gcur[i] = gnext[i];
+      }
+      if (s + 2 < nsub) {
+        if (DMA) load_A(s + 2, a1);
+        load_x(s + 2, xnext, gnext);
       }
     }
   }

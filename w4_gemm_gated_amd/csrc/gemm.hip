@@ -133,14 +133,15 @@ __device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t 
 // the chunk is issued before the first is used (one memory round trip), P's
 // device-coherent when the same launch produced it.  Ends with a block-wide
 // barrier.
-template <int TM, int TN, bool FUSED>
+template <int TM, int TN, bool FUSED, int THREADS>
 __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m0, int n0, unsigned char* lds,
                                                __amdgpu_buffer_rsrc_t pr) {
-  constexpr int kPUnits = TM * (kEcChunk / 4) / kGemmThreads;   // 16-byte P units per thread
+  constexpr int kPUnits = TM * (kEcChunk / 4) / THREADS;   // 16-byte P units per thread
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  constexpr int kBUnits = kEcChunk * TN / 8 / kGemmThreads;   // 16-byte B units per thread
-  static_assert(kEcChunk * TN / 8 % kGemmThreads == 0, "whole B units per thread");
+  constexpr int kBUnits = kEcChunk * TN / 8 / THREADS;   // 16-byte B units per thread
+  static_assert(kEcChunk * TN / 8 % THREADS == 0, "whole B units per thread");
+  static_assert(TM * (kEcChunk / 4) % THREADS == 0, "whole P units per thread");
   half_t* bs = reinterpret_cast<half_t*>(lds);
   half_t* pg = reinterpret_cast<half_t*>(lds + ec_pg_offset<TN>());
   const float* gs = reinterpret_cast<const float*>(lds + ec_gs_offset<TM, TN>());
@@ -151,12 +152,12 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
   if (bvec) {
 #pragma unroll
     for (int i = 0; i < kBUnits; ++i) {
-      const int idx = i * kGemmThreads + tid, r = idx / (TN / 8), c8 = idx % (TN / 8);
+      const int idx = i * THREADS + tid, r = idx / (TN / 8), c8 = idx % (TN / 8);
       bv[i] = *reinterpret_cast<const u32x4_t*>(a.B + (size_t)min(j0 + r, a.rank - 1) * a.N +
                                                  min(n0 + c8 * 8, a.N - 8));
     }
   } else {
-    for (int idx = tid; idx < kEcChunk * TN; idx += kGemmThreads) {
+    for (int idx = tid; idx < kEcChunk * TN; idx += THREADS) {
       const int r = idx / TN, c = idx % TN;
       bs[idx] = a.B[(size_t)min(j0 + r, a.rank - 1) * a.N + min(n0 + c, a.N - 1)];
     }
@@ -164,7 +165,7 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
   float4_t pv[kPUnits];
 #pragma unroll
   for (int i = 0; i < kPUnits; ++i) {
-    const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
+    const int idx = i * THREADS + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
     const int row = min(m0 + r, a.M - 1), col = j0 + c4 * 4;
     const uint32_t off = col < a.ps ? (uint32_t)(((size_t)row * a.ps + col) * 4) : kOutOfRange;
     pv[i] = FUSED ? buffer_load_f4_dev(pr, off)
@@ -172,11 +173,11 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
   }
   if (bvec) {
 #pragma unroll
-    for (int i = 0; i < kBUnits; ++i) reinterpret_cast<u32x4_t*>(bs)[i * kGemmThreads + tid] = bv[i];
+    for (int i = 0; i < kBUnits; ++i) reinterpret_cast<u32x4_t*>(bs)[i * THREADS + tid] = bv[i];
   }
 #pragma unroll
   for (int i = 0; i < kPUnits; ++i) {
-    const int idx = i * kGemmThreads + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
+    const int idx = i * THREADS + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
     const float gv = gs[r];
     half_t* dst = pg + (size_t)r * kEcChunk + c4 * 4;
 #pragma unroll
@@ -190,18 +191,32 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
 // tiles of small M, where the steps are short; two otherwise.
 constexpr int stages_for(int tm, bool split) { return split && tm == 64 ? 3 : 2; }
 
+// Waves side by side with uneven column panels (TP > 0): eight waves, each
+// 128 rows of a 128 x 448 tile; waves 0-3 own four 16-column panels each
+// (panels 0-15), waves 4-7 three (panels 16-27).  Waves are dealt to the
+// four SIMDs of a CU round-robin, so each SIMD runs one wave of four panels
+// and one of three: seven panels of matrix work per SIMD, two waves to issue
+// it.
+__device__ __forceinline__ int uneven_first_panel(int w) { return w < 4 ? 4 * w : 16 + 3 * (w - 4); }
+
 // One GEMM workgroup (tile block `block`).  Wave tile MBW x NBW blocks of
-// 16 x 16; workgroup WM x WN waves.  SPLIT: K split over a.S workgroups per
-// tile.  FUSED: P and g come from EC workgroups of the same launch; the
-// epilogue waits for their ready flags (raised to `tag`) and reads P and g
-// with device-coherent loads.
-template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool FUSED, bool G>
+// 16 x 16; workgroup WM x WN waves (four, or eight with TP = 28 panels per
+// tile dealt unevenly: see uneven_first_panel).  SPLIT: K split over a.S
+// workgroups per tile.  FUSED: P and g come from EC workgroups of the same
+// launch; the epilogue waits for their ready flags (raised to `tag`) and
+// reads P and g with device-coherent loads.
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool FUSED, bool G, int TP = 0>
 __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsigned char* lds, uint32_t tag) {
-  static_assert(WM * WN * kWave == kGemmThreads, "four waves");
+  constexpr int NW = WM * WN;
+  constexpr int THREADS = NW * kWave;
+  constexpr bool UNEVEN = TP != 0;
+  static_assert(!UNEVEN ? NW == 4 : (WM == 1 && WN == 8 && NBW == 4 && TP == 28 && !SPLIT && !FUSED),
+                "four waves, or eight with uneven panels");
+  constexpr int TPANELS = UNEVEN ? TP : NBW * WN;           // 16-column panels per tile
   constexpr int TM = 16 * MBW * WM;
-  constexpr int TN = 16 * NBW * WN;
+  constexpr int TN = 16 * TPANELS;
   constexpr int kStageHalves = TM * kKt;                    // one X stage
-  constexpr int kCopiesPerWave = TM * kUnitsPerRow / kWave / 4;
+  constexpr int kCopiesPerWave = TM * kUnitsPerRow / kWave / NW;
   constexpr int NSTAGE = stages_for(TM, SPLIT);             // X stages in LDS
   half_t* xs = reinterpret_cast<half_t*>(lds);                // [NSTAGE][TM][kKt], swizzled units
 
@@ -226,7 +241,13 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       n_tile = bid % a.NT;
     }
   }
-  const int m0 = m_tile * TM, nb_base = n_tile * (NBW * WN) + wn * NBW;
+  // The wave's panels within the tile: [pan0, pan0 + NBW), or with uneven
+  // panels [pan0, pan0 + 4) for waves 0-3 and [pan0, pan0 + 3) for 4-7;
+  // has(nb): the wave owns its nb-th panel (wave-uniform).
+  const int pan0 = UNEVEN ? uneven_first_panel(w) : wn * NBW;
+  const bool four = !UNEVEN || w < 4;
+  auto has = [&](int nb) { return !UNEVEN || nb < 3 || four; };
+  const int m0 = m_tile * TM, nb_base = n_tile * TPANELS + pan0;
   uint32_t early[4];
   ec_flags_early<TM, FUSED>(a, m0, early);
 
@@ -274,6 +295,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   auto load_w = [&](int kc, u32x4_t* dst) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
+      if (!has(nb)) continue;
       const uint32_t voff = ((uint32_t)min(nb_base + nb, a.NBLK - 1) * (uint32_t)a.KC * 64u + (uint32_t)lane) * 16u;
       dst[nb] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, kc * 1024, 0));
     }
@@ -284,7 +306,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   const int ncol0 = nb_base * 16 + c16;
   auto load_s = [&](int kc, half_t* dst) {
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) dst[nb] = a.scales[(size_t)kc * a.NBLK * 16 + min(ncol0 + nb * 16, a.N - 1)];
+    for (int nb = 0; nb < NBW; ++nb)
+      if (has(nb)) dst[nb] = a.scales[(size_t)kc * a.NBLK * 16 + min(ncol0 + nb * 16, a.N - 1)];
   };
 
   float4_t acc[MBW][NBW];
@@ -309,6 +332,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       }
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
+        if (!has(nb)) continue;
         const half8_t bf = G ? decode_w4(w_[nb][j]) * sg[nb] : decode_w4(w_[nb][j]);
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = mfma16x16x32(af[mb], bf, acc[mb][nb]);
@@ -348,7 +372,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     // Past the last step the copies repeat the last chunk into a stage
     // nothing reads again, so every step issues the same L copies.
     constexpr int kPanels = NBW * WN;                       // per workgroup
-    constexpr int kWCopies = (kPanels + WM * WN - 1) / (WM * WN);   // per wave
+    constexpr int kWCopies = (kPanels + NW - 1) / NW;       // per wave
     // G: one 4-byte copy per lane (lanes 0..31: the wave's 64 group scales,
     // its NBW panels, from the row of chunk kc, N padded to 16) into its own
     // 256-byte slot per stage, ssm[stage][wave][128 halves].
@@ -417,7 +441,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   if (SPLIT && a.S > 1) {
     __shared__ uint32_t ticket;
     const int tile = m_tile * a.NT + n_tile;
-    const uint32_t slice = (uint32_t)MBW * NBW * kGemmThreads * 16;   // bytes of one partial
+    const uint32_t slice = (uint32_t)MBW * NBW * THREADS * 16;   // bytes of one partial
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, (uint32_t)((size_t)tiles * a.S * slice));
     const uint32_t own = (uint32_t)(tile * a.S + split) * slice;
 #pragma unroll
@@ -425,7 +449,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[mb][nb]), pr,
-                                               own + (uint32_t)((mb * NBW + nb) * kGemmThreads + tid) * 16u, 0,
+                                               own + (uint32_t)((mb * NBW + nb) * THREADS + tid) * 16u, 0,
                                                kCachePolicySc1);
     drain_vm();
     __syncthreads();
@@ -452,7 +476,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
 #pragma unroll
           for (int nb = 0; nb < NBW; ++nb)
             v[q][mb][nb] = buffer_load_f4_dev(
-                pr, in ? base + (uint32_t)((mb * NBW + nb) * kGemmThreads + tid) * 16u : kOutOfRange);
+                pr, in ? base + (uint32_t)((mb * NBW + nb) * THREADS + tid) * 16u : kOutOfRange);
       }
 #pragma unroll
       for (int q = 0; q < SB; ++q)
@@ -475,6 +499,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   if (!G) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
+      if (!has(nb)) continue;
       const float s = (float)a.scales[min((nb_base + nb) * 16 + c16, a.N - 1)];
 #pragma unroll
       for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] *= s;
@@ -494,14 +519,15 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((size_t)a.M * a.ps * 4));
   const int n0 = n_tile * TN;
   for (int j0 = 0; j0 < jblocks * 32; j0 += kEcChunk) {
-    ec_stage_chunk<TM, TN, FUSED>(a, j0, m0, n0, lds, pr);
+    ec_stage_chunk<TM, TN, FUSED, THREADS>(a, j0, m0, n0, lds, pr);
     if (any_gate) {
       const int jbn = min(kEcChunk, jblocks * 32 - j0) / 32;
       for (int jb = 0; jb < jbn; ++jb) {
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-          // B operand rows jb*32 + 8 t4 .. + 7 of column (wn NBW + nb) 16 + c16.
-          const half8_t bb = lds_b_fragment_tr(bs + (size_t)jb * 32 * TN + (wn * NBW + nb) * 16, TN, lane);
+          if (!has(nb)) continue;
+          // B operand rows jb*32 + 8 t4 .. + 7 of column (pan0 + nb) 16 + c16.
+          const half8_t bb = lds_b_fragment_tr(bs + (size_t)jb * 32 * TN + (pan0 + nb) * 16, TN, lane);
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
             const int r = wm * MBW * 16 + mb * 16 + c16;
@@ -521,17 +547,19 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   half_t* ys = reinterpret_cast<half_t*>(lds);
   __syncthreads();                             // every wave is done with the epilogue LDS
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
+  for (int nb = 0; nb < NBW; ++nb) {
+    if (!has(nb)) continue;
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        ys[(wm * MBW * 16 + mb * 16 + 4 * t4 + v) * YS + (wn * NBW + nb) * 16 + c16] = (half_t)acc[mb][nb][v];
+        ys[(wm * MBW * 16 + mb * 16 + 4 * t4 + v) * YS + (pan0 + nb) * 16 + c16] = (half_t)acc[mb][nb][v];
+  }
   __syncthreads();
   const int rows = min(TM, a.M - m0);
   if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) {
     const int cols8 = min(TN, a.N - n0) / 8;
-    for (int idx = tid; idx < rows * (TN / 8); idx += kGemmThreads) {
+    for (int idx = tid; idx < rows * (TN / 8); idx += THREADS) {
       const int r = idx / (TN / 8), c8 = idx % (TN / 8);
       if (c8 < cols8)
         *reinterpret_cast<u32x4_t*>(a.Y + (size_t)(m0 + r) * a.N + n0 + c8 * 8) =
@@ -539,7 +567,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     }
   } else {
     const int cols = min(TN, a.N - n0);
-    for (int idx = tid; idx < rows * TN; idx += kGemmThreads) {
+    for (int idx = tid; idx < rows * TN; idx += THREADS) {
       const int r = idx / TN, c = idx % TN;
       if (c < cols) a.Y[(size_t)(m0 + r) * a.N + n0 + c] = ys[r * YS + c];
     }
@@ -558,10 +586,10 @@ constexpr size_t lds_bytes_for() {
   return m > y_tile ? m : y_tile;
 }
 
-template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G>
-__global__ void __launch_bounds__(kGemmThreads) w4_gemm_tiled_kernel(GemmKArgs a) {
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G, int TP>
+__global__ void __launch_bounds__(WM * WN * kWave) w4_gemm_tiled_kernel(GemmKArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  gemm_block<MBW, NBW, WM, WN, SPLIT, false, G>(a, blockIdx.x, lds, 0u);
+  gemm_block<MBW, NBW, WM, WN, SPLIT, false, G, TP>(a, blockIdx.x, lds, 0u);
 }
 
 // Fused tiled launch: blocks [0, E) are EC workgroups (the first ec_blocks
@@ -586,14 +614,15 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs 
   if (threadIdx.x < kWave) count_out(f.sync, gridDim.x, tag);
 }
 
-template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G>
+template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G, int TP = 0>
 hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
-  constexpr size_t lds = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, stages_for(16 * MBW * WM, SPLIT)>();
-  const hipError_t attr =
-      set_max_dynamic_lds(reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT, G>), (int)lds);
+  constexpr size_t lds =
+      lds_bytes_for<16 * MBW * WM, 16 * (TP ? TP : NBW * WN), stages_for(16 * MBW * WM, SPLIT)>();
+  const hipError_t attr = set_max_dynamic_lds(
+      reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT, G, TP>), (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT, G>), dim3((unsigned)(k.MT * k.NT * k.S)),
-                     dim3(kGemmThreads), lds, (hipStream_t)stream, k);
+  hipLaunchKernelGGL((w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT, G, TP>), dim3((unsigned)(k.MT * k.NT * k.S)),
+                     dim3(WM * WN * kWave), lds, (hipStream_t)stream, k);
   return hipGetLastError();
 }
 
@@ -626,13 +655,15 @@ hipError_t launch_fused(const FusedKArgs& f, void* stream) {
 template <bool G>
 hipError_t launch_tiles(const GemmKArgs& k, const FusedKArgs* f, const TiledShape& t, void* stream) {
   if (f) {
+    if (t.tn == 448) return launch_fused<8, 7, 1, 4, false, G>(*f, stream);
     if (t.tm == 256 && t.tn == 224) return launch_fused<8, 7, 2, 2, false, G>(*f, stream);
     if (t.tm == 256) return launch_fused<8, 8, 2, 2, false, G>(*f, stream);
     if (t.tm == 128) return launch_fused<4, 4, 2, 2, true, G>(*f, stream);
     return launch_fused<2, 4, 2, 2, true, G>(*f, stream);
   }
-  // 256-row tiles never split; the mid-size tiles are built with the split
+  // The large tiles never split; the mid-size tiles are built with the split
   // path, which they skip when S is 1.
+  if (t.tn == 448) return launch_cfg<8, 4, 1, 8, false, G, 28>(k, stream);
   if (t.tm == 256 && t.tn == 224) return launch_cfg<8, 7, 2, 2, false, G>(k, stream);
   if (t.tm == 256) return launch_cfg<8, 8, 2, 2, false, G>(k, stream);
   if (t.tm == 128) return launch_cfg<4, 4, 2, 2, true, G>(k, stream);
@@ -642,16 +673,26 @@ hipError_t launch_tiles(const GemmKArgs& k, const FusedKArgs* f, const TiledShap
 }  // namespace
 
 TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_base) {
-  // Large M: 256-row tiles (224 columns when that gives whole waves of 256
-  // tiles), no split.  Mid-size M, where those tiles would not fill the GPU:
+  // Large M: 128 x 448 tiles (four waves side by side, each 128 x 112) when
+  // N fills whole 448-column tiles, else 256-row tiles (224 columns when that
+  // gives whole waves of 256 tiles), no split.  The 128 x 448 tile has the
+  // same wave tile as the 256 x 224 one but copies half the X bytes per step
+  // and decodes each packed word once per workgroup instead of twice
+  // (prefill 2048 x 4096 x 14336, EC off: 186-188 us vs 204-205 us).
+  // Mid-size M, where those tiles would not fill the GPU:
   // 128 x 128 tiles (M > 256) or 64 x 128 tiles, with K split so that about
   // one workgroup per CU runs, each split at least four 128-k chunks.  (At
   // M = 256 the 64-row tiles need no K split where 128-row ones need two:
   // measured 12-22 % faster there, 25 % slower at M = 512 with K = 14336.)
   TiledShape t;
   const int64_t nblk = n_pad(N) / 16, KC = k_pad(K) / kKChunk;
-  t.tm = 256;
-  t.tn = (nblk % 14 == 0 && nblk >= 14) ? 224 : 256;
+  if (nblk % 28 == 0) {
+    t.tm = 128;
+    t.tn = 448;
+  } else {
+    t.tm = 256;
+    t.tn = (nblk % 14 == 0 && nblk >= 14) ? 224 : 256;
+  }
   int64_t tiles = ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16);
   if (tiles < (int64_t)cus * 3 / 4) {
     t.tm = M > 256 ? 128 : 64;
