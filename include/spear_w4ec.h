@@ -277,7 +277,7 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
  * capture, serving loops that forbid allocation).  Same arguments and result
  * as spear_w4ec_linear minus workspace and workspace_bytes; it allocates
  * nothing (no hipMalloc, no allocating library call).  Its workspace is the
- * library's own device array of SPEAR_NOALLOC_WORKSPACE_BYTES (32 MiB) per GPU,
+ * library's own device array of SPEAR_NOALLOC_WORKSPACE_BYTES (64 MiB) per GPU,
  * kept until the process ends; its address is looked up on the first call on
  * each device, which also enqueues on `stream` a small kernel that zeroes the
  * array's 1 MiB header before the call.  That first call must not be made
@@ -289,7 +289,7 @@ spear_status_t spear_w4ec_linear(const spear_linear_desc_t* desc, const spear_pl
  * Errors: as spear_w4ec_linear; WORKSPACE_TOO_SMALL when the plan needs more
  * than SPEAR_NOALLOC_WORKSPACE_BYTES (nothing is enqueued then).
  */
-#define SPEAR_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+#define SPEAR_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
 spear_status_t spear_w4ec_linear_noalloc(const spear_linear_desc_t* desc, const spear_plan_t* plan,
                                          const void* X, const void* Wq, const void* scales,
                                          const void* A, const void* B, const void* w_g, void* Y,

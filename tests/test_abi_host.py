@@ -112,12 +112,14 @@ def test_dispatch_rules(lib):
     # XCD order): 1 row tile x 14 K slices -> 16
     st, p = plan(lib, 64, 14336, 4096, 64)
     assert st == 0 and p.variant == 1 and p.producers == 14 and p.grid == 16 + 32 * p.split_k
-    # 128-row tiles that alone exceed the CUs: auto takes split; where the
-    # tiles fit, fused (even when its EC workgroups overflow the CUs)
+    # 128 x 256 tiles at mid-size M: fused, also when its EC workgroups
+    # overflow the CUs; the K split fills about one workgroup per CU
     st, p = plan(lib, 512, 4096, 14336, 64)
-    assert st == 0 and p.variant == 2 and p.tile_m == 128 and p.grid > 256
+    assert st == 0 and p.variant == 1 and p.tile_m == 128 and p.tile_n == 256 and p.grid > 256
     st, p = plan(lib, 512, 14336, 4096, 64)
-    assert st == 0 and p.variant == 1 and p.tile_m == 128 and p.grid > 256
+    assert st == 0 and p.variant == 1 and p.tile_m == 128 and p.tile_n == 256 and p.grid > 256
+    st, p = plan(lib, 512, 14336, 4096, 64, variant=2)
+    assert st == 0 and p.variant == 2 and p.tile_n == 256 and p.split_k == 4 and p.grid == 4 * 16 * 4
     st, p = plan(lib, 256, 2048, 8192, 32)
     assert st == 0 and p.variant == 1 and p.tile_m == 64
     st, p = plan(lib, 16, 4096, 4096, 32)

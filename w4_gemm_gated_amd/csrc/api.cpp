@@ -114,7 +114,7 @@ const char* spear_status_str(spear_status_t status) {
     case SPEAR_ERR_INVALID_SHAPE: return "SPEAR_ERR_INVALID_SHAPE: need M >= 0, K >= 8, K % 8 == 0, N >= 1, 0 <= rank <= 256";
     case SPEAR_ERR_UNSUPPORTED: return "SPEAR_ERR_UNSUPPORTED: request outside what the kernels implement";
     case SPEAR_ERR_MISALIGNED: return "SPEAR_ERR_MISALIGNED: X, Wq and workspace need 16-byte, fp16 tensors 2-byte alignment";
-    case SPEAR_ERR_WORKSPACE_TOO_SMALL: return "SPEAR_ERR_WORKSPACE_TOO_SMALL: workspace_bytes < plan.workspace_bytes (spear_w4ec_linear_noalloc: the plan needs more than its 32 MiB)";
+    case SPEAR_ERR_WORKSPACE_TOO_SMALL: return "SPEAR_ERR_WORKSPACE_TOO_SMALL: workspace_bytes < plan.workspace_bytes (spear_w4ec_linear_noalloc: the plan needs more than its 64 MiB)";
     case SPEAR_ERR_INVALID_PLAN: return "SPEAR_ERR_INVALID_PLAN: plan does not match the descriptor or this library";
     case SPEAR_ERR_HIP: return "SPEAR_ERR_HIP: the HIP runtime reported an error";
     case SPEAR_ERR_INVALID_ARGUMENT: return "SPEAR_ERR_INVALID_ARGUMENT: non-finite bias, tau outside [0, 1] or unknown variant";

@@ -658,7 +658,7 @@ hipError_t launch_tiles(const GemmKArgs& k, const FusedKArgs* f, const TiledShap
     if (t.tn == 448) return launch_fused<8, 7, 1, 4, false, G>(*f, stream);
     if (t.tm == 256 && t.tn == 224) return launch_fused<8, 7, 2, 2, false, G>(*f, stream);
     if (t.tm == 256) return launch_fused<8, 8, 2, 2, false, G>(*f, stream);
-    if (t.tm == 128) return launch_fused<4, 4, 2, 2, true, G>(*f, stream);
+    if (t.tm == 128) return launch_fused<8, 4, 1, 4, true, G>(*f, stream);
     return launch_fused<2, 4, 2, 2, true, G>(*f, stream);
   }
   // The large tiles never split; the mid-size tiles are built with the split
@@ -666,7 +666,7 @@ hipError_t launch_tiles(const GemmKArgs& k, const FusedKArgs* f, const TiledShap
   if (t.tn == 448) return launch_cfg<8, 4, 1, 8, false, G, 28>(k, stream);
   if (t.tm == 256 && t.tn == 224) return launch_cfg<8, 7, 2, 2, false, G>(k, stream);
   if (t.tm == 256) return launch_cfg<8, 8, 2, 2, false, G>(k, stream);
-  if (t.tm == 128) return launch_cfg<4, 4, 2, 2, true, G>(k, stream);
+  if (t.tm == 128) return launch_cfg<8, 4, 1, 4, true, G>(k, stream);
   return launch_cfg<2, 4, 2, 2, true, G>(k, stream);
 }
 
@@ -680,10 +680,14 @@ TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_
   // and decodes each packed word once per workgroup instead of twice
   // (prefill 2048 x 4096 x 14336, EC off: 186-188 us vs 204-205 us).
   // Mid-size M, where those tiles would not fill the GPU:
-  // 128 x 128 tiles (M > 256) or 64 x 128 tiles, with K split so that about
-  // one workgroup per CU runs, each split at least four 128-k chunks.  (At
-  // M = 256 the 64-row tiles need no K split where 128-row ones need two:
-  // measured 12-22 % faster there, 25 % slower at M = 512 with K = 14336.)
+  // 128 x 256 tiles (M > 256; four waves of 128 x 64 side by side) or
+  // 64 x 128 tiles, with K split so that about one workgroup per CU runs,
+  // each split at least four 128-k chunks.  (At M = 256 the 64-row tiles need
+  // no K split where 128-row ones need two: measured 12-22 % faster there,
+  // 25 % slower at M = 512 with K = 14336.  The 128 x 256 tiles replaced
+  // 2 x 2 waves of 64 x 64 on 128 x 128: EC off 71-73 -> 60-61 us at M = 512,
+  // K = 14336, N = 4096, fused 92-99 -> 83-84; 64 x 256 tiles for M <= 256
+  // measured slower than 64 x 128, 15.0 -> 17.6 us at 256 x 2048 x 2048.)
   TiledShape t;
   const int64_t nblk = n_pad(N) / 16, KC = k_pad(K) / kKChunk;
   if (nblk % 28 == 0) {
@@ -696,7 +700,7 @@ TiledShape tiled_shape(int64_t M, int64_t K, int64_t N, int cus, size_t scratch_
   int64_t tiles = ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16);
   if (tiles < (int64_t)cus * 3 / 4) {
     t.tm = M > 256 ? 128 : 64;
-    t.tn = 128;
+    t.tn = t.tm == 128 ? 256 : 128;
     tiles = ceil_div(M, t.tm) * ceil_div(nblk, t.tn / 16);
     int64_t S = cus / tiles;
     const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(KC / 4, t.tm == 64 ? 16 : 8));

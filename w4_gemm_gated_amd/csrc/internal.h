@@ -186,7 +186,7 @@ TiledShape fused_tiled_shape(int64_t M, int64_t K, int64_t N, int cus, int ec_bl
 // The allocation-free entry point's workspace: a file-scope device array of
 // this size (noalloc.hip), one per GPU; static_scratch returns the current
 // device's address, setting it up on first use (its header zeroed on `stream`).
-constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 hipError_t static_scratch(void** out, void* stream);
 
 // Raise a kernel's dynamic-LDS limit on the current device (once per kernel

@@ -7,16 +7,15 @@
 //   * AUTO and rank % 4 == 0                     -> FUSED: one launch (EC
 //     workgroups first, then the W4 GEMM with the gated epilogue, which
 //     waits for the EC results it needs; at M <= 16 the EC computed by every
-//     GEMM workgroup itself when A is small), except 128 x 128 tiles whose
-//     fused launch would exceed the CUs (M of about 257 to 1024) and the
-//     128 x 448 tiles, where the measured crossover favours SPLIT;
+//     GEMM workgroup itself when A is small), except on the 128 x 448 tiles,
+//     where the measured crossover favours SPLIT;
 //   * AUTO otherwise (rank % 4 != 0)             -> SPLIT (EC projection
 //     launch, then the W4 GEMM with the gated epilogue);
 //   * the per-token gate-value decision (skip the EC term where every gate of
 //     a wave's rows is below tau) is taken on the device in the epilogue.
 //   * main kernel family by M: skinny (M <= 16 rows) or tiled (128 x 448 or
-//     256-row tiles; 128 x 128 or 64-row tiles with K split where those would
-//     not fill the GPU).
+//     256-row tiles; 128 x 256 or 64 x 128 tiles with K split where those
+//     would not fill the GPU).
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -48,8 +47,8 @@ spear_status_t check_desc(const spear_linear_desc_t& d) {
 // L2 (column tiles x M x K x 2 bytes).
 // Tiled kernels: a plain read of B bytes in one launch takes 1.65 us + B / 7.2
 // TB/s (8 MiB .. 256 MiB); matrix rates: the 128 x 448 tiles reach 1.28 PF/s on
-// the prefill shape, the 256-row tiles 1.13, the 128 x 128 and 64-row tiles
-// 0.87 and 0.55 (mid-size M, K split); EC cost of the fused tiles 4 us plus the EC workgroups' read of X
+// the prefill shape, the 256-row tiles 1.13, the 128 x 256 and 64-row tiles
+// 1.0 and 0.55 (mid-size M, K split); EC cost of the fused tiles 4 us plus the EC workgroups' read of X
 // (1.3 TB/s, partly under the GEMM), of the split variant one more launch plus
 // its read of X and its flops.
 // Decode kernel (fitted to 120 calls: ten layer shapes, M = 1, 4, 8, 16, the
@@ -64,7 +63,7 @@ namespace {
 struct CostConstants {
   double stream_bytes_per_us = 7.2e6, skinny_stream_bytes_per_us = 4.06e6, skinny_x_l2_bytes_per_us = 18.95e6;
   double launch_skinny_us = 2.46, launch_tiled_us = 3.0;
-  double mma_skinny = 0.26e9, mma_64 = 0.55e9, mma_128 = 0.87e9, mma_256 = 1.13e9, mma_448 = 1.28e9;   // flop per us
+  double mma_skinny = 0.26e9, mma_64 = 0.55e9, mma_128 = 1.0e9, mma_256 = 1.13e9, mma_448 = 1.28e9;   // flop per us
   double split_skinny_us = 1.91, split_tiled_us = 3.0;
   double ec_handoff_us = 2.04, ec_handoff_per_producer_us = 0.063, ec_handoff_per_kentry_us = 0.131,
          ec_handoff_per_row_us = 0.018;
@@ -138,22 +137,19 @@ spear_status_t make_plan(const spear_linear_desc_t& d, int cus, spear_plan_t* pl
     const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank, kEcBlocksFused);
     return L.m_tiles <= kMaxEcTiles;
   };
-  // Measured crossover (mid M, hot weights, 128 EC workgroups): with
-  // 128-row tiles that alone exceed the CUs the split variant is faster
-  // (M = 512, K = 4096, N = 14336: 87 vs 94 us); where the tiles fit, the
-  // fused one is, also when its EC workgroups overflow the CUs (M = 512,
-  // K = 14336, N = 4096: 98 vs 104 us; M = 768: 153 vs 161; M = 1024: 163 vs
-  // 172; M = 1024, K = N = 4096: 57 vs 61; M = 512, K = 2048, N = 8192: a
-  // tie), as with 64-row (M <= 256) and 256-row tiles.  On 128 x 448 tiles
-  // the split variant runs the eight-wave tile kernel, which only the split
-  // and EC-off launches have (M = 2048, K = 4096, N = 14336: split 200-213 us
-  // vs fused 211-220 over four boxes).
+  // Measured crossover (cold weights, 128 EC workgroups): on 128 x 256
+  // tiles (M of about 257 to 1024) the fused variant is faster (M = 512,
+  // K = 4096, N = 14336: 65 vs 71 us; M = 512, K = 14336, N = 4096: 83-84 vs
+  // 85; M = 1024, K = N = 4096: 51 vs 55), as with 64-row (M <= 256) and
+  // 256-row tiles.  On 128 x 448 tiles the split variant runs the eight-wave
+  // tile kernel, which only the split and EC-off launches have (M = 2048,
+  // K = 4096, N = 14336: split 200-213 us vs fused 211-220 over four boxes).
   auto split_wins = [&]() {
     if (skinny) return false;
     const EcWorkspace L = ec_workspace_layout(d.M, d.K, d.rank, kEcBlocksFused);
     const int eb = (int)round_up(L.m_tiles * L.splits, 8);
     const TiledShape t = fused_tiled_shape(d.M, d.K, d.N, cus, eb, kSyncHeaderBytes);
-    return (t.tm == 128 && t.tn == 128 && t.grid > cus) || t.tn == 448;
+    return t.tn == 448;
   };
   if (!ec) {
     p.variant = SPEAR_VARIANT_NO_EC;
