@@ -129,13 +129,13 @@ __device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t 
 }
 
 // Stage rank columns [j0, j0 + 64) of the EC operands: bs (16-byte loads
-// when B rows are 16-byte aligned, else element-wise) and pg; every load of
-// the chunk is issued before the first is used (one memory round trip), P's
-// device-coherent when the same launch produced it.  Ends with a block-wide
-// barrier.
+// when B rows are 16-byte aligned, else element-wise; b_ready: already
+// copied there by copy_b_chunk) and pg; every load of the chunk is issued
+// before the first is used (one memory round trip), P's device-coherent when
+// the same launch produced it.  Ends with a block-wide barrier.
 template <int TM, int TN, bool FUSED, int THREADS>
 __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m0, int n0, unsigned char* lds,
-                                               __amdgpu_buffer_rsrc_t pr) {
+                                               __amdgpu_buffer_rsrc_t pr, bool b_ready = false) {
   constexpr int kPUnits = TM * (kEcChunk / 4) / THREADS;   // 16-byte P units per thread
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -149,7 +149,8 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
   __syncthreads();
   const bool bvec = a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0;
   u32x4_t bv[kBUnits];
-  if (bvec) {
+  if (b_ready) {
+  } else if (bvec) {
 #pragma unroll
     for (int i = 0; i < kBUnits; ++i) {
       const int idx = i * THREADS + tid, r = idx / (TN / 8), c8 = idx % (TN / 8);
@@ -171,7 +172,7 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
     pv[i] = FUSED ? buffer_load_f4_dev(pr, off)
                   : __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
   }
-  if (bvec) {
+  if (bvec && !b_ready) {
 #pragma unroll
     for (int i = 0; i < kBUnits; ++i) reinterpret_cast<u32x4_t*>(bs)[i * THREADS + tid] = bv[i];
   }
@@ -187,9 +188,35 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
   __syncthreads();
 }
 
+// B rows [j0, j0 + 64) of the tile's columns straight into bs[64][TN] by
+// direct 16-byte buffer-to-LDS copies (B rows 16-byte aligned, N % 8 == 0):
+// copy i of wave w fills the 64 units (i NW + w) 64 .. + 63 of bs, unit u
+// holding B[min(j0 + u / (TN / 8), rank - 1)][n0 + 8 (u % (TN / 8))]
+// (columns past N read as zeros and are never stored).  Nothing waits for
+// the copies here; ec_stage_chunk's final wait and barrier do.
+template <int TN, int THREADS>
+__device__ __forceinline__ void copy_b_chunk(const GemmKArgs& a, int j0, int n0, unsigned char* bs_lds) {
+  constexpr int NW = THREADS / kWave;
+  constexpr int kUnits = kEcChunk * TN / 8;
+  static_assert(kUnits % THREADS == 0, "whole copies per wave");
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.B, (uint32_t)((size_t)a.rank * a.N * 2));
+#pragma unroll
+  for (int i = 0; i < kUnits / THREADS; ++i) {
+    const int u0 = (i * NW + w) * kWave, u = u0 + lane;
+    const int r = u / (TN / 8), c = n0 + (u % (TN / 8)) * 8;
+    const uint32_t voff = c < a.N ? (uint32_t)(((size_t)min(j0 + r, a.rank - 1) * a.N + c) * 2) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void_t*)(bs_lds + (size_t)u0 * 16), 16, voff, 0, 0, 0);
+  }
+}
+
 // X stages of a tile kernel: three (loads two steps ahead) for the 64-row
 // tiles of small M, where the steps are short; two otherwise.
 constexpr int stages_for(int tm, bool split) { return split && tm == 64 ? 3 : 2; }
+// Epilogue LDS after the X stages (the first B chunk copied in during the
+// last k-step): 128-row tiles without a K split, where both fit.
+constexpr bool epilogue_after_stages(int tm, bool split) { return tm == 128 && !split; }
 
 // Waves side by side with uneven column panels (TP > 0): eight waves, each
 // 128 rows of a 128 x 448 tile; waves 0-3 own four 16-column panels each
@@ -219,6 +246,10 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   constexpr int kCopiesPerWave = TM * kUnitsPerRow / kWave / NW;
   constexpr int NSTAGE = stages_for(TM, SPLIT);             // X stages in LDS
   half_t* xs = reinterpret_cast<half_t*>(lds);                // [NSTAGE][TM][kKt], swizzled units
+  // 128-row tiles without a K split keep the epilogue's LDS past the X
+  // stages, so the first B chunk can be copied in during the last k-step.
+  constexpr bool PREF = epilogue_after_stages(TM, SPLIT);
+  unsigned char* epi = lds + (PREF ? (size_t)NSTAGE * kStageHalves * 2 : 0);
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -339,6 +370,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
       }
     }
   };
+  const bool b_pref = PREF && a.ec && a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0;
   if (NSTAGE == 2) {
     // Two stages, loads one step ahead (the 256-row tiles: two X stages fill
     // the LDS).
@@ -355,6 +387,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
         issue_x(kc + 1, st ^ 1);
         load_w(kc + 1, wnext);
         if (G) load_s(kc + 1, snext);
+      } else if (b_pref) {
+        copy_b_chunk<TN, THREADS>(a, 0, n_tile * TN, epi);
       }
       compute(st, wcur, scur);
 #pragma unroll
@@ -506,9 +540,9 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     }
   }
   const int jblocks = a.ec ? a.ps / 32 : 0;
-  const half_t* bs = reinterpret_cast<const half_t*>(lds);
-  const half_t* pg = reinterpret_cast<const half_t*>(lds + ec_pg_offset<TN>());
-  float* gs = reinterpret_cast<float*>(lds + ec_gs_offset<TM, TN>());
+  const half_t* bs = reinterpret_cast<const half_t*>(epi);
+  const half_t* pg = reinterpret_cast<const half_t*>(epi + ec_pg_offset<TN>());
+  float* gs = reinterpret_cast<float*>(epi + ec_gs_offset<TM, TN>());
   bool any_gate = false;
   if (jblocks > 0) {
     ec_prepare<TM, FUSED>(a, m0, tag, gs, early);
@@ -519,7 +553,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((size_t)a.M * a.ps * 4));
   const int n0 = n_tile * TN;
   for (int j0 = 0; j0 < jblocks * 32; j0 += kEcChunk) {
-    ec_stage_chunk<TM, TN, FUSED, THREADS>(a, j0, m0, n0, lds, pr);
+    ec_stage_chunk<TM, TN, FUSED, THREADS>(a, j0, m0, n0, epi, pr, b_pref && j0 == 0);
     if (any_gate) {
       const int jbn = min(kEcChunk, jblocks * 32 - j0) / 32;
       for (int jb = 0; jb < jbn; ++jb) {
@@ -574,13 +608,18 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   }
 }
 
-template <int TM, int TN, int NS>
+template <int TM, int TN, bool SPLIT>
 constexpr size_t lds_bytes_for() {
   // X stages, and with three stages the packed-weight stages (TN / 16 panels
-  // of 1 KiB each, one copy per wave at least).
+  // of 1 KiB each, one copy per wave at least); the epilogue's B chunk, g' P
+  // and gates overlay them, or follow them (epilogue_after_stages).
+  constexpr int NS = stages_for(TM, SPLIT);
   constexpr size_t w_stages = NS == 3 ? (size_t)3 * ((TN / 16 + 3) / 4 * 4) * 1024 + (size_t)3 * 4 * kWave * 4 : 0;
   constexpr size_t stages = (size_t)NS * TM * kKt * 2 + w_stages;
-  constexpr size_t epilogue = (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
+  constexpr size_t epilogue =
+      epilogue_after_stages(TM, SPLIT)
+          ? stages + (size_t)kEcChunk * TN * 2 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4
+          : (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
   constexpr size_t y_tile = (size_t)TM * (TN + 8) * 2;
   constexpr size_t m = stages > epilogue ? stages : epilogue;
   return m > y_tile ? m : y_tile;
@@ -617,7 +656,7 @@ __global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G, int TP = 0>
 hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
   constexpr size_t lds =
-      lds_bytes_for<16 * MBW * WM, 16 * (TP ? TP : NBW * WN), stages_for(16 * MBW * WM, SPLIT)>();
+      lds_bytes_for<16 * MBW * WM, 16 * (TP ? TP : NBW * WN), SPLIT>();
   const hipError_t attr = set_max_dynamic_lds(
       reinterpret_cast<const void*>(&w4_gemm_tiled_kernel<MBW, NBW, WM, WN, SPLIT, G, TP>), (int)lds);
   if (attr != hipSuccess) return attr;
@@ -628,7 +667,7 @@ hipError_t launch_cfg(const GemmKArgs& k, void* stream) {
 
 template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB, bool G>
 hipError_t launch_fused_pb(const FusedKArgs& f, void* stream) {
-  const size_t tile = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, stages_for(16 * MBW * WM, SPLIT)>();
+  const size_t tile = lds_bytes_for<16 * MBW * WM, 16 * NBW * WN, SPLIT>();
   const size_t ec = ec_lds_bytes(f.e.ss, f.e.rp);
   const size_t lds = tile > ec ? tile : ec;
   if (ec_kb_for(PB) * 32 != f.e.ss || lds > kMaxLdsBytes - 1024) return hipErrorInvalidValue;
