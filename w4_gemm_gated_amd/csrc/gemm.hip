@@ -105,7 +105,7 @@ __device__ __forceinline__ void ec_flags_early(const GemmKArgs& a, int m0, uint3
 // block-wide barrier.
 template <int TM, bool FUSED>
 __device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t tag, float* gs,
-                                           const uint32_t (&early)[4]) {
+                                           const uint32_t (&early)[4], bool gs_ready = false) {
   const int tid = threadIdx.x;
   if (FUSED && tid == 0) {
     const int t_end = min(a.ec_tiles, (m0 + TM + 63) / 64);
@@ -123,19 +123,23 @@ __device__ __forceinline__ void ec_prepare(const GemmKArgs& a, int m0, uint32_t 
       }
     }
   }
+  if (gs_ready) wait_vm_all();                 // this wave's copies into gs (copy_ec_rows) have landed
   __syncthreads();                             // also: every wave is done with the X stages
-  if (tid < TM) gs[tid] = m0 + tid < a.M ? (FUSED ? ld_dev(&a.g[m0 + tid]) : a.g[m0 + tid]) : 0.0f;
+  if (!gs_ready && tid < TM) gs[tid] = m0 + tid < a.M ? (FUSED ? ld_dev(&a.g[m0 + tid]) : a.g[m0 + tid]) : 0.0f;
   __syncthreads();
 }
 
 // Stage rank columns [j0, j0 + 64) of the EC operands: bs (16-byte loads
 // when B rows are 16-byte aligned, else element-wise; b_ready: already
-// copied there by copy_b_chunk) and pg; every load of the chunk is issued
-// before the first is used (one memory round trip), P's device-coherent when
-// the same launch produced it.  Ends with a block-wide barrier.
+// copied there by copy_b_chunk) and pg (p_lds: the chunk's P units already
+// copied into LDS by copy_ec_rows, unit u at p_lds + 16 u); every load of the
+// chunk is issued before the first is used (one memory round trip), P's
+// device-coherent when the same launch produced it.  Ends with a block-wide
+// barrier.
 template <int TM, int TN, bool FUSED, int THREADS>
 __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m0, int n0, unsigned char* lds,
-                                               __amdgpu_buffer_rsrc_t pr, bool b_ready = false) {
+                                               __amdgpu_buffer_rsrc_t pr, bool b_ready = false,
+                                               const unsigned char* p_lds = nullptr) {
   constexpr int kPUnits = TM * (kEcChunk / 4) / THREADS;   // 16-byte P units per thread
   const int tid = threadIdx.x, lane = tid % kWave;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -169,7 +173,8 @@ __device__ __forceinline__ void ec_stage_chunk(const GemmKArgs& a, int j0, int m
     const int idx = i * THREADS + tid, r = idx / (kEcChunk / 4), c4 = idx % (kEcChunk / 4);
     const int row = min(m0 + r, a.M - 1), col = j0 + c4 * 4;
     const uint32_t off = col < a.ps ? (uint32_t)(((size_t)row * a.ps + col) * 4) : kOutOfRange;
-    pv[i] = FUSED ? buffer_load_f4_dev(pr, off)
+    pv[i] = p_lds ? *reinterpret_cast<const float4_t*>(p_lds + (size_t)idx * 16)
+          : FUSED ? buffer_load_f4_dev(pr, off)
                   : __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
   }
   if (bvec && !b_ready) {
@@ -208,6 +213,35 @@ __device__ __forceinline__ void copy_b_chunk(const GemmKArgs& a, int j0, int n0,
     const int r = u / (TN / 8), c = n0 + (u % (TN / 8)) * 8;
     const uint32_t voff = c < a.N ? (uint32_t)(((size_t)min(j0 + r, a.rank - 1) * a.N + c) * 2) : kOutOfRange;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void_t*)(bs_lds + (size_t)u0 * 16), 16, voff, 0, 0, 0);
+  }
+}
+
+// P rank columns [0, 64) of the tile's rows and their gates, from an earlier
+// launch (the split variant), straight into LDS: unit u = 16 r + c4 of P (row
+// m0 + r clamped to M - 1, columns 4 c4 .. + 3; columns past the stride read
+// as zeros) at p_lds + 16 u, the unit layout ec_stage_chunk reads, and
+// g'[m0 + r] at gs + 4 r (rows past M read as zeros) by the first TM / 64
+// waves.  Nothing waits for the copies here.
+template <int TM, int THREADS>
+__device__ __forceinline__ void copy_ec_rows(const GemmKArgs& a, int m0, unsigned char* p_lds, float* gs) {
+  constexpr int NW = THREADS / kWave;
+  constexpr int kUnits = TM * (kEcChunk / 4);
+  static_assert(kUnits % THREADS == 0 && TM % kWave == 0 && TM / kWave <= NW, "whole copies per wave");
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((size_t)a.M * a.ps * 4));
+#pragma unroll
+  for (int i = 0; i < kUnits / THREADS; ++i) {
+    const int u0 = (i * NW + w) * kWave, u = u0 + lane;
+    const int r = u / (kEcChunk / 4), col = (u % (kEcChunk / 4)) * 4;
+    const uint32_t voff = col < a.ps ? (uint32_t)(((size_t)min(m0 + r, a.M - 1) * a.ps + col) * 4) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_void_t*)(p_lds + (size_t)u0 * 16), 16, voff, 0, 0, 0);
+  }
+  if (w < TM / kWave) {
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.g, (uint32_t)a.M * 4u);
+    const int row = m0 + w * kWave + lane;
+    const uint32_t voff = row < a.M ? (uint32_t)row * 4u : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void_t*)(gs + w * kWave), 4, voff, 0, 0, 0);
   }
 }
 
@@ -371,6 +405,8 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
     }
   };
   const bool b_pref = PREF && a.ec && a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0;
+  float* gs_pre = reinterpret_cast<float*>(epi + ec_gs_offset<TM, TN>());
+  int p_stage = 0;                             // the X stage that holds the copied P (b_pref, split variant)
   if (NSTAGE == 2) {
     // Two stages, loads one step ahead (the 256-row tiles: two X stages fill
     // the LDS).
@@ -388,7 +424,11 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
         load_w(kc + 1, wnext);
         if (G) load_s(kc + 1, snext);
       } else if (b_pref) {
+        p_stage = st ^ 1;
         copy_b_chunk<TN, THREADS>(a, 0, n_tile * TN, epi);
+        // The split variant's P and g' (an earlier launch): P into the X
+        // stage this step does not read, g' into gs.
+        if (!FUSED) copy_ec_rows<TM, THREADS>(a, m0, lds + (size_t)(st ^ 1) * kStageHalves * 2, gs_pre);
       }
       compute(st, wcur, scur);
 #pragma unroll
@@ -545,7 +585,7 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   float* gs = reinterpret_cast<float*>(epi + ec_gs_offset<TM, TN>());
   bool any_gate = false;
   if (jblocks > 0) {
-    ec_prepare<TM, FUSED>(a, m0, tag, gs, early);
+    ec_prepare<TM, FUSED>(a, m0, tag, gs, early, b_pref && !FUSED);
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) any_gate |= gs[wm * MBW * 16 + mb * 16 + c16] != 0.0f;
     any_gate = __any(any_gate);
@@ -553,7 +593,9 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.P, (uint32_t)((size_t)a.M * a.ps * 4));
   const int n0 = n_tile * TN;
   for (int j0 = 0; j0 < jblocks * 32; j0 += kEcChunk) {
-    ec_stage_chunk<TM, TN, FUSED, THREADS>(a, j0, m0, n0, epi, pr, b_pref && j0 == 0);
+    ec_stage_chunk<TM, TN, FUSED, THREADS>(a, j0, m0, n0, epi, pr, b_pref && j0 == 0,
+                                           b_pref && !FUSED && j0 == 0 ? lds + (size_t)p_stage * kStageHalves * 2
+                                                                       : nullptr);
     if (any_gate) {
       const int jbn = min(kEcChunk, jblocks * 32 - j0) / 32;
       for (int jb = 0; jb < jbn; ++jb) {
