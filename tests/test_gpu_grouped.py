@@ -103,11 +103,13 @@ def test_grouped_prefill_workload(variant):
 @pytest.mark.parametrize("variant", ["fused", "split"])
 @pytest.mark.parametrize("M,K,N,r", [(3, 136, 20, 4), (16, 2056, 4096, 32), (5, 8192, 256, 64), (1, 1000, 100, 20),
                                      (17, 264, 40, 4), (130, 392, 200, 32), (300, 1000, 100, 20),
-                                     (520, 2056, 300, 36), (2100, 1000, 7000, 36), (64, 14336, 4096, 64)])
+                                     (520, 2056, 300, 36), (2100, 1000, 7000, 36), (64, 14336, 4096, 64),
+                                     (1000, 200, 10750, 64)])
 def test_grouped_ragged_shapes(M, K, N, r, variant):
     """K tails (the last group shorter than 128), partial column panels, every
     tile path: decode (local EC and hand-off), 64-row tiles with K split (three
-    stages, scales through LDS), 128-row tiles, 256-row tiles."""
+    stages, scales through LDS), 128 x 256 tiles, 256-row tiles, 128 x 448
+    tiles (four waves fused, eight waves split)."""
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=11 * M + K + N + r, outliers=True)
     if variant == "fused" and r % 4 != 0:
         pytest.skip("the fused variant needs rank % 4 == 0")
