@@ -661,14 +661,23 @@ constexpr size_t lds_bytes_for() {
   constexpr size_t epilogue =
       epilogue_after_stages(TM, SPLIT)
           ? stages + (size_t)kEcChunk * TN * 2 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4
-          : (size_t)kEcChunk * TN * 4 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
+          : (size_t)kEcChunk * TN * 2 + (size_t)TM * kEcChunk * 2 + (size_t)TM * 4;
   constexpr size_t y_tile = (size_t)TM * (TN + 8) * 2;
   constexpr size_t m = stages > epilogue ? stages : epilogue;
   return m > y_tile ? m : y_tile;
 }
 
+// Waves per SIMD a kernel is built for: two for the 128-row mid-size tiles
+// (128 x 256 with a K split), so that two workgroups share a CU (256
+// registers per wave, under 80 KiB of LDS each) and, in the fused launch, the
+// leading EC workgroups do not keep GEMM workgroups off the CUs they hold
+// (mixed-gate down_proj M = 512, K = 14336, N = 4096, fused: 84-88 -> 71-78
+// us; M = 1024, K = N = 4096: 50-55 -> 45 us; EC off unchanged).
+constexpr int waves_per_simd(int tm, bool split) { return split && tm == 128 ? 2 : 1; }
+
 template <int MBW, int NBW, int WM, int WN, bool SPLIT, bool G, int TP>
-__global__ void __launch_bounds__(WM * WN * kWave) w4_gemm_tiled_kernel(GemmKArgs a) {
+__global__ void __launch_bounds__(WM * WN * kWave, waves_per_simd(16 * MBW * WM, SPLIT))
+    w4_gemm_tiled_kernel(GemmKArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   gemm_block<MBW, NBW, WM, WN, SPLIT, false, G, TP>(a, blockIdx.x, lds, 0u);
 }
@@ -682,7 +691,8 @@ __global__ void __launch_bounds__(WM * WN * kWave) w4_gemm_tiled_kernel(GemmKArg
 // itself out last (count_out: the last to finish returns the finisher count
 // to zero and advances the epoch; every block has read it by then).
 template <int MBW, int NBW, int WM, int WN, bool SPLIT, int PB, bool G>
-__global__ void __launch_bounds__(kGemmThreads) w4_gemm_fused_kernel(FusedKArgs f) {
+__global__ void __launch_bounds__(kGemmThreads, waves_per_simd(16 * MBW * WM, SPLIT))
+    w4_gemm_fused_kernel(FusedKArgs f) {
   extern __shared__ __align__(16) unsigned char lds[];
   const uint32_t tag = call_tag(f.sync);
   const int b = blockIdx.x;
