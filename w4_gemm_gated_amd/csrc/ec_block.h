@@ -54,6 +54,7 @@ struct EcKArgs {
   float* g_out;
   float gate_bias, skip_tau;
   uint32_t* ready;       // fused launch: [m_tiles] flags set to the call's tag; else null
+  int partials_only;     // stop after the slice's partials (a second launch adds the slices)
 };
 
 inline int ec_rank_pad(int64_t rank) { return (int)round_up(rank, 4); }
@@ -77,6 +78,7 @@ inline EcKArgs make_ec_kargs(const EcArgs& e, const EcWorkspace& L) {
   a.zero_pad = e.P_out ? 0 : 1;
   a.gate_bias = e.gate_bias; a.skip_tau = e.skip_tau;
   a.ready = nullptr;
+  a.partials_only = 0;
   return a;
 }
 
@@ -318,6 +320,7 @@ __device__ __forceinline__ void ec_block(const EcKArgs& a, unsigned char* lds, i
       }
     }
   }
+  if (a.partials_only) return;                // ec_slices_kernel adds the slices
   drain_vm();
   __syncthreads();
   if (tid == 0) {
