@@ -283,6 +283,23 @@ def test_large_tile_ragged_shapes(M, K, N, r, variant):
     layer_case(X, W, A, B, w_g, -0.5, 0.0, variant, f"large-tile {variant} M={M} K={K} N={N} r={r}")
 
 
+@pytest.mark.parametrize("variant", ["fused", "split"])
+@pytest.mark.parametrize("M,K,N,r,tau", [(1000, 200, 10750, 20, 0.0), (1000, 256, 10752, 96, 0.0),
+                                         (1000, 200, 10750, 64, 0.6)])
+def test_large_tile_ec_edges(M, K, N, r, tau, variant):
+    """128 x 448 tiles, where the first EC chunk's B (and, split variant, P
+    and the gates) reach the LDS during the last k-step: a rank whose P
+    stride is 32 (columns 32-63 of the chunk read as zeros), a rank of two
+    EC chunks (the second staged in the epilogue), and a skip threshold with
+    gates on both sides of it; every element of Y."""
+    X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=5 * M + K + N + r, outliers=True)
+    if variant == "fused" and r % 4 != 0:
+        pytest.skip("the fused variant needs rank % 4 == 0")
+    p = sp.spear_dispatch_plan(M, K, N, r, 0.3, tau, variant=variant)
+    assert p.tile_m == 128 and p.tile_n == 448
+    layer_case(X, W, A, B, w_g, 0.3, tau, variant, f"large-tile EC {variant} M={M} K={K} N={N} r={r} tau={tau}")
+
+
 def test_empty_batch():
     w = workloads.workload(1)
     Wq_d, s_d = sp.spear_pack_w4(cuda(w["W"]))
