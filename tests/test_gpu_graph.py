@@ -29,7 +29,7 @@ def cuda(a):
 
 @pytest.mark.parametrize("noalloc", [False, True])
 @pytest.mark.parametrize("M,K,N,r", [(4, 4096, 4096, 32), (16, 8192, 1024, 64), (3, 1024, 4096, 16),
-                                     (130, 392, 200, 32), (512, 2048, 2048, 64)])
+                                     (130, 392, 200, 32), (512, 2048, 2048, 64), (1000, 256, 10752, 64)])
 def test_graph_replay_matches_eager(M, K, N, r, noalloc):
     X, W, A, B, w_g = workloads.random_layer(M, K, N, r, seed=M + K + N + r + 17, outliers=True)
     Wq, s = sp.spear_pack_w4(cuda(W))
