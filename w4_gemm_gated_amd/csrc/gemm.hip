@@ -291,13 +291,23 @@ __device__ __forceinline__ void gemm_block(const GemmKArgs& a, int block, unsign
   const int wm = w % WM, wn = w / WM;
 
   // Tile order: with a multiple of 8 row tiles, XCD x (block % 8) takes row
-  // tiles x, x + 8, ... and walks the column tiles of each.
+  // tiles x, x + 8, ... and walks the column tiles of each; with a multiple
+  // of 16 it takes them in pairs (x + 16 i, x + 16 i + 8) whose two tiles of
+  // one column run side by side, so each packed-weight tile the XCD fetches
+  // serves two workgroups from its L2 (prefill 2048 x 4096 x 14336, A/B on
+  // one box each: EC off 186-189 -> 182-184 us and 197-199 -> 195-198 us;
+  // g128 unchanged).
   int m_tile, n_tile;
   const int tiles = a.MT * a.NT;
   const int split = block / tiles;
   {
     const int bid = block % tiles;
-    if (a.MT % 8 == 0) {
+    if (a.MT % 16 == 0) {
+      const int xcd = bid % 8, j = bid / 8;
+      const int pair = j / (2 * a.NT), r = j % (2 * a.NT);
+      m_tile = xcd + 8 * (2 * pair + r % 2);
+      n_tile = r / 2;
+    } else if (a.MT % 8 == 0) {
       const int xcd = bid % 8, j = bid / 8;
       m_tile = xcd + 8 * (j / a.NT);
       n_tile = j % a.NT;
